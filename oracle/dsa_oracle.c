@@ -1,0 +1,464 @@
+/*
+ * dsa_oracle.c -- CPU oracle for the pooled-key DSA indexer and sparse NoPE-MLA decode.
+ *
+ * TEST INFRASTRUCTURE ONLY. The tests, the package smoke check and the CPU-baseline leg of
+ * the benchmark load this file's shared object; the GPU library never does, and this file
+ * shares no source, header, table or helper with it.
+ *
+ * Plain and slow on purpose: one loop nest per definition, every floating-point step in
+ * double, results rounded once to the output type (f32, or bf16 by round-to-nearest-even of
+ * the f32 value, the rounding the upload path of build.rs uses). The absorb transforms are
+ * the exception: they follow the f32 arithmetic and loop order that build.rs gives for them.
+ * Built with -O2 -ffp-contract=off, no fast-math. The only parallelism is an OpenMP loop
+ * over independent output rows, which changes no arithmetic.
+ *
+ * Sources (documentation pages of metrale_model_arch::glm5next_dsa):
+ *   mod.rs   -- module doc "Shape of the pipeline" and "Checkpoint and kernel facts",
+ *               Glm5NextDsaConfig::{select_k, out_width, validate}
+ *   build.rs -- module doc "The transforms", absorb_q_rows, absorb_q, absorb_o
+ *   tp.rs    -- module doc "Why the indexer is replicated" (the index score rule)
+ * Where the pages leave a step open, the reading taken is stated at the function.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- number formats */
+
+/* bf16 is the top half of an IEEE binary32. */
+static double bf16_value(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* binary32 -> bf16, round to nearest, ties to even (NaN kept quiet). */
+static uint16_t bf16_from_float(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t keep = u >> 16;
+    uint32_t rest = u & 0xffffu;
+    if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;
+    return (uint16_t)keep;
+}
+
+/* OCP 8-bit floating point, E4M3 ("FN": no infinities, S.1111.111 is NaN):
+ * sign bit 7, exponent bits 6..3 with bias 7, mantissa bits 2..0; exponent field 0 is
+ * subnormal, value mantissa/8 * 2^-6. */
+static double e4m3_value(uint8_t c) {
+    int sign = (c >> 7) & 1, ex = (c >> 3) & 15, man = c & 7;
+    double v;
+    if (ex == 15 && man == 7) return NAN;
+    if (ex == 0) v = ldexp((double)man / 8.0, -6);
+    else v = ldexp(1.0 + (double)man / 8.0, ex - 7);
+    return sign ? -v : v;
+}
+
+/* f64 result rounded once to f32; a zero of either sign comes back as +0. */
+static float to_f32_canonical(double x) {
+    float f = (float)x;
+    if (f == 0.0f) f = 0.0f;
+    return f;
+}
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+double orc_bf16_value(uint16_t h) { return bf16_value(h); }
+double orc_e4m3_value(uint8_t c) { return e4m3_value(c); }
+uint16_t orc_bf16_from_float(float f) { return bf16_from_float(f); }
+
+/* ---------------------------------------------------------------- geometry + validation */
+
+/* Glm5NextDsaConfig::select_k (mod.rs): pools selected per query, the pool budget
+ * index_topk / index_kpool capped by the number of pools. */
+long orc_select_k(long index_topk, long index_kpool, long n_pools) {
+    long k = index_topk / index_kpool;
+    return k < n_pools ? k : n_pools;
+}
+
+/* Glm5NextDsaConfig::out_width (mod.rs): index row width is index_topk, with
+ * index_kpool - 1 extra tail slots when always_select_tail is set. */
+long orc_out_width(long index_topk, long index_kpool, int always_select_tail) {
+    return index_topk + (always_select_tail ? index_kpool - 1 : 0);
+}
+
+/* Number of whole pools in S token slots when pooling starts at first_key (mod.rs,
+ * "Checkpoint and kernel facts": pooling starts at first_key and a trailing partial pool is
+ * not a pool). With first_key = 0 this is tp.rs's seq / kpool. */
+long orc_num_pools(long S, long first_key, long kpool) {
+    if (kpool <= 0 || S <= first_key) return 0;
+    return (S - first_key) / kpool;
+}
+
+/* Glm5NextDsaConfig::validate (mod.rs), its six refusals in the page's order.
+ * Returns 0 when the config is accepted, else the 1-based number of the first failing
+ * rule: 1 kpool or topk zero, 2 topk not a multiple of kpool, 3 kpool above the 8-slot
+ * kernel bound, 4 kv_lora_rank zero, 5 kv_lora_rank not the 512 the decode kernel is built
+ * for, 6 no attention heads on this rank. */
+int orc_validate(long index_kpool, long index_topk, long kv_lora_rank, long local_heads) {
+    if (index_kpool == 0 || index_topk == 0) return 1;
+    if (index_topk % index_kpool != 0) return 2;
+    if (index_kpool > 8) return 3;
+    if (kv_lora_rank == 0) return 4;
+    if (kv_lora_rank != 512) return 5;
+    if (local_heads == 0) return 6;
+    return 0;
+}
+
+/* ---------------------------------------------------------------- step 1: kpool_compress */
+
+/* mod.rs, "Shape of the pipeline" (k, gate, valid, ape -> pool keys / indices / valid) and
+ * "Checkpoint and kernel facts" (softmax over the pool-slot axis, per channel; pooling starts
+ * at first_key; a pool counts only if all index_kpool slots are valid). build.rs transform 4:
+ * ape is f32.
+ * Reading: pool p of sequence b covers tokens t_s = first_key + p*KP + s, s < KP. For each
+ * channel d the slot weights are softmax_s(gate[b,t_s,d] + ape[s,d]) and the pooled key is
+ * the weighted sum of k[b,t_s,d]; it is stored as bf16. The pool index p itself is the pool's
+ * identity (its first token is first_key + p*KP), so no separate index array is written.
+ * Layouts: k, gate [B,S,D] bf16; ape [KP,D] f32; valid [B,S] u8;
+ * pool_keys [B,P,D] bf16; pool_valid [B,P] u8, with P = orc_num_pools(S, first_key, KP). */
+void orc_kpool_compress(int B, int S, int D, int KP, int first_key,
+                        const uint16_t *k, const uint16_t *gate, const float *ape,
+                        const uint8_t *valid, uint16_t *pool_keys, uint8_t *pool_valid) {
+    long P = orc_num_pools(S, first_key, KP);
+    long bp;
+#pragma omp parallel for schedule(static)
+    for (bp = 0; bp < (long)B * P; ++bp) {
+        long b = bp / P, p = bp % P;
+        long t0 = (long)first_key + p * KP;
+        int ok = 1;
+        for (int s = 0; s < KP; ++s)
+            if (!valid[b * S + t0 + s]) ok = 0;
+        pool_valid[b * P + p] = (uint8_t)ok;
+        for (int d = 0; d < D; ++d) {
+            double logit[64], mx = -INFINITY, den = 0.0, acc = 0.0;
+            for (int s = 0; s < KP; ++s) {
+                logit[s] = bf16_value(gate[(b * S + t0 + s) * D + d]) + (double)ape[s * D + d];
+                if (logit[s] > mx) mx = logit[s];
+            }
+            for (int s = 0; s < KP; ++s) den += exp(logit[s] - mx);
+            for (int s = 0; s < KP; ++s)
+                acc += (exp(logit[s] - mx) / den) * bf16_value(k[(b * S + t0 + s) * D + d]);
+            pool_keys[(b * P + p) * D + d] = bf16_from_float((float)acc);
+        }
+    }
+}
+
+/* ---------------------------------------------------------------- step 2: compact_pools */
+
+/* mod.rs names dsa_compact_pools between pooling and scoring and says no more.
+ * Reading: a stable compaction. ids[b, 0..n_valid[b]) are the valid pool indices of sequence
+ * b in ascending order, the remaining entries are -1; n_valid[b] is their count.
+ * Layouts: pool_valid [B,P] u8; ids [B,P] i32; n_valid [B] i32. */
+void orc_compact_pools(int B, int P, const uint8_t *pool_valid, int32_t *ids, int32_t *n_valid) {
+    for (long b = 0; b < B; ++b) {
+        int32_t n = 0;
+        for (long p = 0; p < P; ++p)
+            if (pool_valid[b * P + p]) ids[b * P + n++] = (int32_t)p;
+        n_valid[b] = n;
+        for (long j = n; j < P; ++j) ids[b * P + j] = -1;
+    }
+}
+
+/* ---------------------------------------------------------------- step 3: index_scores */
+
+/* tp.rs, "Why the indexer is replicated": a pool's score adds weights[h] * relu(scale * dot)
+ * over the indexer heads, giving [q_rows, n_pools] scores. build.rs transform 2: the
+ * index_heads^-0.5 factor is already folded into the weights, the scorer does not apply it.
+ * mod.rs, "Shape of the pipeline": the output is the score array plus candidate validity.
+ * Readings: w is given per query row and head ([Q,Hi] f32, already scaled). The dot is
+ * q[r,h,:] . key[b,p,:] with b = row_seq[r]; for fp8 keys the dot of the decoded e4m3 values
+ * is multiplied by the pool's f32 scale. A pool is a candidate for row r when it is listed in
+ * the compacted valid list of its sequence and its last token first_key + (p+1)*KP - 1 is at
+ * or before the row's position row_pos[r] (decode rows sit at the last valid token, prefill
+ * rows are causal). Heads are summed in ascending order in double; the f32 result has
+ * -0 turned into +0. Non-candidate slots get -inf and cand = 0.
+ * Layouts: q [Q,Hi,D] bf16; w [Q,Hi] f32; row_seq/row_pos [Q] i32; keys [B,P,D] bf16 or e4m3
+ * (key_fp8 = 1) with key_scales [B,P] f32; ids [B,P], n_valid [B] i32;
+ * scores [Q,P] f32; cand [Q,P] u8. */
+void orc_index_scores(int Q, int B, int P, int Hi, int D, int KP, int first_key, double scale,
+                      const uint16_t *q, const float *w, const int32_t *row_seq,
+                      const int32_t *row_pos, const void *keys, int key_fp8,
+                      const float *key_scales, const int32_t *ids, const int32_t *n_valid,
+                      float *scores, uint8_t *cand) {
+    (void)B;
+    long r;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < Q; ++r) {
+        long b = row_seq[r], pos = row_pos[r];
+        for (long p = 0; p < P; ++p) {
+            scores[r * P + p] = -INFINITY;
+            cand[r * P + p] = 0;
+        }
+        for (long j = 0; j < n_valid[b]; ++j) {
+            long p = ids[b * P + j];
+            long last_token = (long)first_key + (p + 1) * KP - 1;
+            if (last_token > pos) continue;
+            double key_scale = key_fp8 ? (double)key_scales[b * P + p] : 1.0;
+            double total = 0.0;
+            for (int h = 0; h < Hi; ++h) {
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d) {
+                    double qv = bf16_value(q[(r * Hi + h) * D + d]);
+                    double kv = key_fp8 ? e4m3_value(((const uint8_t *)keys)[(b * P + p) * D + d])
+                                        : bf16_value(((const uint16_t *)keys)[(b * P + p) * D + d]);
+                    dot += qv * kv;
+                }
+                double x = scale * (key_scale * dot);
+                total += (double)w[r * Hi + h] * (x > 0.0 ? x : 0.0);
+            }
+            scores[r * P + p] = to_f32_canonical(total);
+            cand[r * P + p] = 1;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------- step 4: topk_pools */
+
+typedef struct { float score; int32_t pool; } scored_pool;
+
+/* Ranking key: higher score first; among equal scores the lower pool index first. */
+static int by_score_then_pool(const void *a, const void *b) {
+    const scored_pool *x = (const scored_pool *)a, *y = (const scored_pool *)b;
+    if (x->score > y->score) return -1;
+    if (x->score < y->score) return 1;
+    return (x->pool > y->pool) - (x->pool < y->pool);
+}
+
+static int by_pool(const void *a, const void *b) {
+    int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* mod.rs, "Shape of the pipeline": topk_pools turns the scores into [Q, select_k] pool ids;
+ * select_k = min(index_topk / index_kpool, n_pools).
+ * Readings: the Kw best candidates by (score descending, pool index ascending) are chosen;
+ * equal scores go to the lower pool index (tp.rs warns that ties at the cutoff are order
+ * sensitive, so the rule is fixed). The chosen ids are written in ascending pool order; a row
+ * with fewer than Kw candidates is padded with -1. Scores compare as floats, so -0 == +0.
+ * Layouts: scores [Q,P] f32; cand [Q,P] u8; sel [Q,Kw] i32. */
+void orc_topk_pools(int Q, int P, int Kw, const float *scores, const uint8_t *cand, int32_t *sel) {
+    long r;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < Q; ++r) {
+        scored_pool *list = (scored_pool *)malloc(sizeof(scored_pool) * (size_t)(P > 0 ? P : 1));
+        int32_t *chosen = (int32_t *)malloc(sizeof(int32_t) * (size_t)(Kw > 0 ? Kw : 1));
+        long n = 0;
+        for (long p = 0; p < P; ++p)
+            if (cand[r * P + p]) {
+                list[n].score = scores[r * P + p];
+                list[n].pool = (int32_t)p;
+                ++n;
+            }
+        qsort(list, (size_t)n, sizeof(scored_pool), by_score_then_pool);
+        long take = n < Kw ? n : Kw;
+        for (long i = 0; i < take; ++i) chosen[i] = list[i].pool;
+        qsort(chosen, (size_t)take, sizeof(int32_t), by_pool);
+        for (long i = 0; i < Kw; ++i) sel[r * Kw + i] = i < take ? chosen[i] : -1;
+        free(list);
+        free(chosen);
+    }
+}
+
+/* ---------------------------------------------------------------- step 5: expand_selection */
+
+/* mod.rs, "Shape of the pipeline" ([Q, out_width] token ids, -1 = invalid) and "Checkpoint
+ * and kernel facts" (-1 goes over the whole row before any index is stored, so every slot is
+ * written); Glm5NextDsaConfig::out_width for the row width.
+ * Readings: selected pool i (sel[r,i] = p >= 0) fills slots i*KP .. i*KP+KP-1 with tokens
+ * first_key + p*KP + s. With always_select_tail the tokens after the last whole pool up to and
+ * including the row's position, t in [tail_start, pos] with
+ * tail_start = first_key + floor((pos + 1 - first_key) / KP) * KP, go to slots
+ * index_topk + (t - tail_start); a tail token that is not valid stays -1.
+ * Layouts: sel [Q,Kw] i32; row_seq/row_pos [Q] i32; valid [B,S] u8; token_ids [Q,W] i32. */
+void orc_expand_selection(int Q, int Kw, int KP, int index_topk, int always_select_tail, int S,
+                          int first_key, const int32_t *sel, const int32_t *row_seq,
+                          const int32_t *row_pos, const uint8_t *valid, int32_t *token_ids) {
+    long W = orc_out_width(index_topk, KP, always_select_tail);
+    for (long r = 0; r < Q; ++r) {
+        int32_t *row = token_ids + r * W;
+        for (long i = 0; i < W; ++i) row[i] = -1;
+        for (long i = 0; i < Kw; ++i) {
+            long p = sel[r * Kw + i];
+            if (p < 0) continue;
+            for (long s = 0; s < KP; ++s) row[i * KP + s] = (int32_t)(first_key + p * KP + s);
+        }
+        if (always_select_tail) {
+            long b = row_seq[r], pos = row_pos[r];
+            if (pos + 1 > first_key) {
+                long tail_start = first_key + ((pos + 1 - first_key) / KP) * KP;
+                for (long t = tail_start; t <= pos; ++t)
+                    if (t < S && valid[b * S + t]) row[index_topk + (t - tail_start)] = (int32_t)t;
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------- step 6: sparse MLA decode */
+
+/* build.rs, "The transforms" (1 and 3): the query is absorbed into the kv_lora_rank-wide latent
+ * space and the decode output is [local_heads, kv_lora_rank] in that space; mod.rs: NoPE (no
+ * rope section), latent width 512, attention restricted to the expanded tokens; the serve
+ * decode reads the selected tokens through a block table.
+ * Readings: for row r and head h, over the row's token ids t >= 0 (in slot order), with v_t
+ * the latent row of token t of sequence b = row_seq[r] (bf16, or e4m3 times the row's f32
+ * scale): logit_t = sm * (q_abs[r,h,:] . v_t), out[r,h,:] = sum_t softmax(logit)_t * v_t;
+ * keys and values are the same latent rows. lse = max + log(sum exp(logit - max)). A row with
+ * no token gives out = 0 and lse = -inf.
+ * Latent row address: contiguous, b*S + t; paged (block_table != NULL),
+ * block_table[b*max_blocks + t/block_size]*block_size + t%block_size. kv_scales (fp8 only)
+ * is indexed by the same row number.
+ * Layouts: q_abs [Q,H,C] bf16; token_ids [Q,W] i32; row_seq [Q] i32; kv [rows,C] bf16/e4m3;
+ * out [Q,H,C] f32; lse [Q,H] f32 (may be NULL). */
+void orc_sparse_mla(int Q, int H, int C, int W, double sm, const uint16_t *q_abs,
+                    const int32_t *token_ids, const int32_t *row_seq, const void *kv, int kv_fp8,
+                    const float *kv_scales, int S, const int32_t *block_table, int max_blocks,
+                    int block_size, float *out, float *lse) {
+    long r;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < Q; ++r) {
+        long b = row_seq[r];
+        long *rows = (long *)malloc(sizeof(long) * (size_t)(W > 0 ? W : 1));
+        double *logit = (double *)malloc(sizeof(double) * (size_t)(W > 0 ? W : 1));
+        double *v = (double *)malloc(sizeof(double) * (size_t)C);
+        long n = 0;
+        for (long i = 0; i < W; ++i) {
+            long t = token_ids[r * W + i];
+            if (t < 0) continue;
+            long row = block_table ? (long)block_table[b * max_blocks + t / block_size] * block_size +
+                                         t % block_size
+                                   : b * (long)S + t;
+            rows[n++] = row;
+        }
+        for (long h = 0; h < H; ++h) {
+            const uint16_t *qh = q_abs + (r * H + h) * C;
+            float *oh = out + (r * H + h) * C;
+            double mx = -INFINITY, den = 0.0;
+            for (long i = 0; i < n; ++i) {
+                double dot = 0.0;
+                for (long c = 0; c < C; ++c) {
+                    double vc = kv_fp8 ? e4m3_value(((const uint8_t *)kv)[rows[i] * C + c]) *
+                                             (double)kv_scales[rows[i]]
+                                       : bf16_value(((const uint16_t *)kv)[rows[i] * C + c]);
+                    dot += bf16_value(qh[c]) * vc;
+                }
+                logit[i] = sm * dot;
+                if (logit[i] > mx) mx = logit[i];
+            }
+            for (long i = 0; i < n; ++i) den += exp(logit[i] - mx);
+            for (long c = 0; c < C; ++c) v[c] = 0.0;
+            for (long i = 0; i < n; ++i) {
+                double pw = exp(logit[i] - mx) / den;
+                for (long c = 0; c < C; ++c) {
+                    double vc = kv_fp8 ? e4m3_value(((const uint8_t *)kv)[rows[i] * C + c]) *
+                                             (double)kv_scales[rows[i]]
+                                       : bf16_value(((const uint16_t *)kv)[rows[i] * C + c]);
+                    v[c] += pw * vc;
+                }
+            }
+            for (long c = 0; c < C; ++c) oh[c] = n ? (float)v[c] : 0.0f;
+            if (lse) lse[r * H + h] = n ? (float)(mx + log(den)) : -INFINITY;
+        }
+        free(rows);
+        free(logit);
+        free(v);
+    }
+}
+
+/* ---------------------------------------------------------------- host weight transforms */
+
+static void put_msg(char *msg, int msg_len, const char *text) {
+    if (msg && msg_len > 0) {
+        strncpy(msg, text, (size_t)msg_len - 1);
+        msg[msg_len - 1] = 0;
+    }
+}
+
+/* build.rs, absorb_q and absorb_q_rows: out[h*kvl + c][k] =
+ * sum over r < nope of kv_b[h*(nope+vd) + r][c] * q_b[h*nope + r][k], in f32 with r ascending,
+ * accumulating acc[k] += q * w (separate multiply and add). Refuses wrong element counts
+ * (q_b must be [heads*(nope+rope), ql], kv_b [heads*(nope+vd), kvl]) and a nonzero rope
+ * width. Returns 0, or 1 (q_b count), 2 (kv_b count), 3 (rope). out is [heads*kvl, ql]. */
+int orc_absorb_q(int heads, int nope, int rope, int vd, int kvl, int ql, const float *q_b,
+                 long q_b_len, const float *kv_b, long kv_b_len, float *out, char *msg,
+                 int msg_len) {
+    if (q_b_len != (long)heads * (nope + rope) * ql) {
+        put_msg(msg, msg_len, "q_b element count does not match heads*qk_head_dim*q_lora_rank");
+        return 1;
+    }
+    if (kv_b_len != (long)heads * (nope + vd) * kvl) {
+        put_msg(msg, msg_len, "kv_b element count does not match heads*(nope+v)*kv_lora_rank");
+        return 2;
+    }
+    if (rope != 0) {
+        put_msg(msg, msg_len, "absorption is defined for NoPE only (rope width must be 0)");
+        return 3;
+    }
+    long rows = (long)heads * kvl;
+    for (long row = 0; row < rows; ++row) {
+        long h = row / kvl, c = row % kvl;
+        float *acc = out + row * ql;
+        for (long k = 0; k < ql; ++k) acc[k] = 0.0f;
+        for (long r = 0; r < nope; ++r) {
+            float wv = kv_b[(h * (nope + vd) + r) * kvl + c];
+            const float *q_row = q_b + (h * nope + r) * ql;
+            for (long k = 0; k < ql; ++k) {
+                float prod = q_row[k] * wv;
+                acc[k] = acc[k] + prod;
+            }
+        }
+    }
+    return 0;
+}
+
+/* build.rs, absorb_o: o_absorb[i][h*kvl + c] =
+ * sum over r < vd of o_proj[i][h*vd + r] * kv_b[h*(nope+vd) + nope + r][c], f32, r ascending,
+ * dst += w * k (separate multiply and add). Refuses a nonzero rope width and wrong counts
+ * (o_local [hidden, heads*vd], kv_b_local [heads*(nope+vd), kvl]). Returns 0, or 3 (rope),
+ * 1 (o_proj count), 2 (kv_b count), checked in that order. out is [hidden, heads*kvl]. */
+int orc_absorb_o(int heads, int nope, int rope, int vd, int kvl, int hidden, const float *o_local,
+                 long o_len, const float *kv_b_local, long kv_len, float *out, char *msg,
+                 int msg_len) {
+    if (rope != 0) {
+        put_msg(msg, msg_len, "absorption is defined for NoPE only (rope width must be 0)");
+        return 3;
+    }
+    long in_w = (long)heads * vd, out_w = (long)heads * kvl;
+    if (o_len != (long)hidden * in_w) {
+        put_msg(msg, msg_len, "o_proj element count does not match hidden*heads*v_head_dim");
+        return 1;
+    }
+    if (kv_len != (long)heads * (nope + vd) * kvl) {
+        put_msg(msg, msg_len, "kv_b element count does not match heads*(nope+v)*kv_lora_rank");
+        return 2;
+    }
+    for (long i = 0; i < (long)hidden * out_w; ++i) out[i] = 0.0f;
+    for (long i = 0; i < hidden; ++i) {
+        for (long h = 0; h < heads; ++h) {
+            float *dst = out + i * out_w + h * kvl;
+            long v_base = h * (nope + vd) + nope;
+            for (long r = 0; r < vd; ++r) {
+                float wv = o_local[i * in_w + h * vd + r];
+                const float *src = kv_b_local + (v_base + r) * kvl;
+                for (long c = 0; c < kvl; ++c) {
+                    float prod = wv * src[c];
+                    dst[c] = dst[c] + prod;
+                }
+            }
+        }
+    }
+    return 0;
+}

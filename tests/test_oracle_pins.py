@@ -1,0 +1,671 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Every test here runs on the host. Each pins one oracle function to something fixed by the
+documentation pages or by mathematics: printed figures (tests/golden/), closed forms,
+invariances, special cases that reduce to a library routine (torch's attention in f64,
+numpy's mean), exact rational arithmetic on dyadic inputs, and brute force on tiny inputs.
+They are chosen so that a dropped term, a wrong softmax axis, a wrong sign or a transposed
+index in the oracle fails at least one of them.
+"""
+from fractions import Fraction
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dsa_pooled_key_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    out = []
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                out.append(line.split())
+    return out
+
+
+def bf16_ulp(x):
+    x = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
+# ------------------------------------------------------------------ number formats
+
+def test_e4m3_decode_matches_ocp_table():
+    for code, value in _rows("e4m3_ocp.txt"):
+        got = oracle.e4m3_value(int(code, 16))
+        if value == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == float(value) and math.copysign(1, got) == math.copysign(1, float(value))
+
+
+def test_e4m3_all_codes_monotone_and_roundtrip_through_encoder():
+    vals = np.array([oracle.e4m3_value(c) for c in range(256)])
+    pos = vals[:127]                       # 0x00..0x7e, non-negative finite
+    assert np.all(np.diff(pos) > 0)
+    assert np.array_equal(vals[128:255], -pos)
+    # the input encoder (independent code) maps every finite value back to its code
+    codes = synth.e4m3_codes(pos.astype(np.float32))
+    assert np.array_equal(codes, np.arange(127, dtype=np.uint8))
+
+
+def test_bf16_roundtrip_and_rne():
+    assert oracle.bf16_value(0x3F80) == 1.0
+    assert oracle.bf16_value(0xC000) == -2.0
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: ties to even keeps 1.0
+    assert oracle.bf16_from_float(1.0 + 2.0 ** -8) == 0x3F80
+    # 1 + 3*2^-8 is a tie between 1+2^-7 (odd) and 1+2^-6 (even)
+    assert oracle.bf16_from_float(1.0 + 3 * 2.0 ** -8) == 0x3F82
+    assert oracle.bf16_from_float(1.0 + 2.0 ** -8 + 2.0 ** -20) == 0x3F81
+
+
+# ------------------------------------------------------------------ geometry + validation
+
+def test_page_figures():
+    fig = {k: int(v) for k, v in _rows("page_figures.txt")}
+    pools = oracle.num_pools(fig["context_tokens"], 0, fig["kpool"])
+    assert pools == fig["pools"]
+    assert pools * np.dtype(np.float32).itemsize == fig["score_bytes_per_token"] == 256 * 1024
+    assert fig["masked_attn_smem_bytes"] // 4 == fig["masked_attn_max_keys"]
+    assert oracle.validate(fig["kernel_max_kpool"], 4096, fig["kernel_kv_lora_dim"], 1) == 0
+    assert oracle.validate(fig["kernel_max_kpool"] + 1, 4104 - 4104 % 9, 512, 1) == 3
+    assert fig["qk_head_dim"] + fig["v_head_dim"] == fig["kv_b_rows_per_head"]
+
+
+def test_validate_rules_in_page_order():
+    for kp, tk, kvl, heads, rule in _rows("validate_cases.txt"):
+        assert oracle.validate(int(kp), int(tk), int(kvl), int(heads)) == int(rule), (kp, tk, kvl)
+
+
+def test_select_k_and_out_width():
+    for tk, kp, n, tail, sk, ow in _rows("geometry_cases.txt"):
+        assert oracle.select_k(int(tk), int(kp), int(n)) == int(sk)
+        assert oracle.out_width(int(tk), int(kp), bool(int(tail))) == int(ow)
+
+
+def test_trailing_partial_pool_and_first_key():
+    assert oracle.num_pools(1024, 0, 4) == 256
+    assert oracle.num_pools(1023, 0, 4) == 255
+    assert oracle.num_pools(1024, 3, 4) == 255
+    assert oracle.num_pools(1024, 4, 4) == 255
+    assert oracle.num_pools(3, 0, 4) == 0
+    assert oracle.num_pools(5, 5, 4) == 0
+
+
+# ------------------------------------------------------------------ kpool_compress
+
+def _kp_case(rng, B, S, D, KP, dyadic=True):
+    if dyadic:
+        k = synth.bf16_bits(rng.integers(-4, 5, (B, S, D)) / 4.0)
+    else:
+        k = synth.bf16_bits(rng.standard_normal((B, S, D)).astype(np.float32))
+    gate = synth.bf16_bits(rng.standard_normal((B, S, D)).astype(np.float32))
+    ape = rng.standard_normal((KP, D)).astype(np.float32)
+    valid = np.ones((B, S), np.uint8)
+    return k, gate, ape, valid
+
+
+def test_kpool_single_slot_is_identity():
+    rng = np.random.default_rng(1)
+    k, gate, _, valid = _kp_case(rng, 2, 37, 16, 1, dyadic=False)
+    ape = rng.standard_normal((1, 16)).astype(np.float32)
+    pk, pv = oracle.kpool_compress(k, gate, ape, valid, 1, 5)
+    assert pk.shape == (2, 32, 16)
+    assert np.array_equal(pk, k[:, 5:])
+    assert pv.all()
+
+
+@pytest.mark.parametrize("KP,f", [(4, 0), (8, 3), (2, 1), (3, 2)])
+def test_kpool_uniform_logits_is_slot_mean(KP, f):
+    rng = np.random.default_rng(KP)
+    B, S, D = 2, 50, 8
+    k, _, _, valid = _kp_case(rng, B, S, D, KP)
+    gate = np.zeros_like(k)
+    ape = np.zeros((KP, D), np.float32)
+    pk, _ = oracle.kpool_compress(k, gate, ape, valid, KP, f)
+    P = (S - f) // KP
+    kf = synth.bf16_to_f32(k).astype(np.float64)
+    want = kf[:, f:f + P * KP].reshape(B, P, KP, D).mean(axis=2)
+    got = synth.bf16_to_f32(pk).astype(np.float64)
+    if KP in (2, 4, 8):     # power-of-two means of quarter values are exact in bf16
+        assert np.array_equal(got, want)
+    else:                   # thirds are inexact: one bf16 ulp, plus f64 residue at a zero mean
+        assert np.all(np.abs(got - want) <= bf16_ulp(want) + 1e-12)
+
+
+def test_kpool_one_hot_ape_picks_a_slot_per_channel():
+    rng = np.random.default_rng(7)
+    B, S, D, KP = 1, 64, 16, 8
+    k, _, _, valid = _kp_case(rng, B, S, D, KP, dyadic=False)
+    gate = np.zeros_like(k)
+    hot = rng.integers(0, KP, D)
+    ape = np.full((KP, D), -64.0, np.float32)
+    ape[hot, np.arange(D)] = 64.0
+    pk, _ = oracle.kpool_compress(k, gate, ape, valid, KP, 0)
+    want = k.reshape(B, S // KP, KP, D)[:, :, hot, np.arange(D)]
+    assert np.array_equal(pk, want)
+
+
+def test_kpool_two_slot_logistic_closed_form():
+    # With two slots the weight of slot 0 is the logistic function of x0 - x1.
+    rng = np.random.default_rng(3)
+    B, S, D, KP = 1, 40, 4, 2
+    k, gate, ape, valid = _kp_case(rng, B, S, D, KP, dyadic=False)
+    pk, _ = oracle.kpool_compress(k, gate, ape, valid, KP, 0)
+    kf = synth.bf16_to_f32(k).astype(np.float64)
+    gf = synth.bf16_to_f32(gate).astype(np.float64)
+    got = synth.bf16_to_f32(pk).astype(np.float64)
+    for p in range(S // 2):
+        for d in range(D):
+            x0 = gf[0, 2 * p, d] + ape[0, d]
+            x1 = gf[0, 2 * p + 1, d] + ape[1, d]
+            s0 = 1.0 / (1.0 + math.exp(x1 - x0))
+            want = s0 * kf[0, 2 * p, d] + (1.0 - s0) * kf[0, 2 * p + 1, d]
+            assert abs(got[0, p, d] - want) <= bf16_ulp(want) + 1e-30
+
+
+def test_kpool_softmax_runs_over_slots_not_channels():
+    # A per-channel constant added to every slot's gate leaves a softmax over slots unchanged
+    # (it would change a softmax over channels); a per-slot constant shared by all channels
+    # changes the result. Dyadic gates keep the shifted values exact in bf16.
+    rng = np.random.default_rng(11)
+    B, S, D, KP = 1, 32, 8, 4
+    k, _, ape, valid = _kp_case(rng, B, S, D, KP)
+    g = rng.integers(-8, 9, (B, S, D)) / 4.0
+    c = rng.integers(-8, 9, D) / 4.0
+    base, _ = oracle.kpool_compress(k, synth.bf16_bits(g), ape, valid, KP, 0)
+    shifted, _ = oracle.kpool_compress(k, synth.bf16_bits(g + c), ape, valid, KP, 0)
+    a = synth.bf16_to_f32(base).astype(np.float64)
+    b = synth.bf16_to_f32(shifted).astype(np.float64)
+    assert np.all(np.abs(a - b) <= bf16_ulp(a))
+    ape2 = ape + np.arange(KP, dtype=np.float32)[:, None] * 3.0
+    moved, _ = oracle.kpool_compress(k, synth.bf16_bits(g), ape2, valid, KP, 0)
+    assert not np.array_equal(moved, base)
+
+
+def test_kpool_validity_brute_force_and_first_key():
+    rng = np.random.default_rng(5)
+    B, S, D, KP, f = 3, 45, 4, 4, 2
+    k, gate, ape, _ = _kp_case(rng, B, S, D, KP)
+    valid = (rng.random((B, S)) > 0.1).astype(np.uint8)
+    pk, pv = oracle.kpool_compress(k, gate, ape, valid, KP, f)
+    P = (S - f) // KP
+    assert pv.shape == (B, P)
+    for b in range(B):
+        for p in range(P):
+            slots = [valid[b, f + p * KP + s] for s in range(KP)]
+            assert pv[b, p] == int(all(slots))
+    # tokens before first_key and after the last whole pool never influence anything
+    k2, g2, v2 = k.copy(), gate.copy(), valid.copy()
+    k2[:, :f] = 0x7F00
+    g2[:, :f] = 0x4100
+    v2[:, :f] = 0
+    tail = f + P * KP
+    k2[:, tail:] = 0x4000
+    v2[:, tail:] = 0
+    pk2, pv2 = oracle.kpool_compress(k2, g2, ape, v2, KP, f)
+    assert np.array_equal(pk, pk2) and np.array_equal(pv, pv2)
+
+
+# ------------------------------------------------------------------ compact_pools
+
+def test_compact_pools_enumeration():
+    rng = np.random.default_rng(0)
+    pv = (rng.random((5, 33)) > 0.4).astype(np.uint8)
+    pv[2] = 0
+    pv[3] = 1
+    ids, nv = oracle.compact_pools(pv)
+    for b in range(5):
+        on = [p for p in range(33) if pv[b, p]]
+        assert nv[b] == len(on)
+        assert list(ids[b, :len(on)]) == on
+        assert np.all(ids[b, len(on):] == -1)
+
+
+# ------------------------------------------------------------------ index_scores
+
+def _score_case(rng, Q, B, P, Hi, D, dyadic=True):
+    if dyadic:
+        q = rng.integers(-4, 5, (Q, Hi, D)) / 4.0
+        keys = rng.integers(-16, 17, (B, P, D)) / 16.0
+        w = rng.integers(-12, 13, (Q, Hi)) / 8.0
+    else:
+        q = rng.standard_normal((Q, Hi, D))
+        keys = rng.standard_normal((B, P, D))
+        w = rng.standard_normal((Q, Hi))
+    return (synth.bf16_bits(q.astype(np.float32)), w.astype(np.float32),
+            synth.bf16_bits(keys.astype(np.float32)))
+
+
+def _all_valid(B, P):
+    return oracle.compact_pools(np.ones((B, P), np.uint8))
+
+
+def test_index_scores_exact_rational_on_dyadic_inputs():
+    rng = np.random.default_rng(21)
+    Q, B, P, Hi, D, KP = 3, 2, 20, 4, 16, 4
+    q, w, keys = _score_case(rng, Q, B, P, Hi, D)
+    ids, nv = _all_valid(B, P)
+    row_seq = np.array([1, 0, 1], np.int32)
+    row_pos = np.array([10 ** 6] * Q, np.int32)
+    scores, cand = oracle.index_scores(q, w, row_seq, row_pos, keys, ids, nv, kpool=KP,
+                                       first_key=0, scale=0.125)
+    assert cand.all()
+    qf, kf = synth.bf16_to_f32(q), synth.bf16_to_f32(keys)
+    for r in range(Q):
+        b = row_seq[r]
+        for p in range(P):
+            tot = Fraction(0)
+            for h in range(Hi):
+                dot = sum(Fraction(float(qf[r, h, d])) * Fraction(float(kf[b, p, d]))
+                          for d in range(D))
+                x = Fraction(1, 8) * dot
+                tot += Fraction(float(w[r, h])) * max(x, Fraction(0))
+            assert scores[r, p] == float(tot), (r, p)
+
+
+def test_index_scores_single_head_closed_form_and_relu():
+    rng = np.random.default_rng(22)
+    Q, B, P, D = 2, 1, 30, 32
+    q, _, keys = _score_case(rng, Q, B, P, 1, D, dyadic=False)
+    w = np.ones((Q, 1), np.float32)
+    ids, nv = _all_valid(B, P)
+    seq = np.zeros(Q, np.int32)
+    pos = np.full(Q, 10 ** 6, np.int32)
+    scale = float(np.float32(32 ** -0.5))
+    s_pos, _ = oracle.index_scores(q, w, seq, pos, keys, ids, nv, kpool=4, first_key=0, scale=scale)
+    s_neg, _ = oracle.index_scores(q ^ np.uint16(0x8000), w, seq, pos, keys, ids, nv, kpool=4,
+                                   first_key=0, scale=scale)
+    dot = np.einsum("rd,pd->rp", synth.bf16_to_f32(q)[:, 0].astype(np.float64),
+                    synth.bf16_to_f32(keys)[0].astype(np.float64))
+    want = np.maximum(scale * dot, 0.0)
+    assert np.allclose(s_pos, want, rtol=1e-6, atol=1e-7)
+    # relu(x) - relu(-x) = x: one of the two is zero for every pool
+    assert np.allclose(s_pos - s_neg, scale * dot, rtol=1e-6, atol=1e-6)
+    assert np.all((s_pos == 0) | (s_neg == 0))
+
+
+def test_index_scores_weight_pairs_with_its_head_and_scales_linearly():
+    rng = np.random.default_rng(23)
+    Q, B, P, Hi, D = 2, 1, 12, 3, 8
+    q, w, keys = _score_case(rng, Q, B, P, Hi, D)
+    ids, nv = _all_valid(B, P)
+    seq = np.zeros(Q, np.int32)
+    pos = np.full(Q, 10 ** 6, np.int32)
+    kw = dict(kpool=4, first_key=0, scale=0.125)
+    base, _ = oracle.index_scores(q, w, seq, pos, keys, ids, nv, **kw)
+    dbl, _ = oracle.index_scores(q, w * 2, seq, pos, keys, ids, nv, **kw)
+    neg, _ = oracle.index_scores(q, -w, seq, pos, keys, ids, nv, **kw)
+    assert np.array_equal(dbl, base * 2)
+    assert np.array_equal(neg, -base + 0.0)
+    # w only on head 1 while q is zero everywhere but head 0 -> score 0
+    q0 = q.copy()
+    q0[:, 1:] = 0
+    w1 = np.zeros_like(w)
+    w1[:, 1] = 1.0
+    z, _ = oracle.index_scores(q0, w1, seq, pos, keys, ids, nv, **kw)
+    assert np.all(z == 0) and not np.any(np.signbit(z))
+    # doubling scale equals doubling q (relu is positively homogeneous)
+    s2, _ = oracle.index_scores(q, w, seq, pos, keys, ids, nv, kpool=4, first_key=0, scale=0.25)
+    q2 = synth.bf16_bits(synth.bf16_to_f32(q) * 2)
+    t2, _ = oracle.index_scores(q2, w, seq, pos, keys, ids, nv, **kw)
+    assert np.array_equal(s2, t2)
+
+
+def test_index_scores_candidacy_causal_and_listed():
+    rng = np.random.default_rng(24)
+    B, P, Hi, D, KP, f = 2, 10, 2, 8, 4, 3
+    q, w, keys = _score_case(rng, 4, B, P, Hi, D)
+    pv = np.ones((B, P), np.uint8)
+    pv[0, [2, 5]] = 0
+    ids, nv = oracle.compact_pools(pv)
+    # pool p's last token is f + (p+1)*KP - 1
+    last6 = f + 7 * KP - 1
+    row_seq = np.array([0, 0, 1, 1], np.int32)
+    row_pos = np.array([last6, last6 - 1, f - 1, 10 ** 6], np.int32)
+    s, c = oracle.index_scores(q, w, row_seq, row_pos, keys, ids, nv, kpool=KP, first_key=f,
+                               scale=0.125)
+    want0 = [p for p in range(P) if pv[0, p] and p <= 6]
+    assert list(np.nonzero(c[0])[0]) == want0
+    assert list(np.nonzero(c[1])[0]) == [p for p in want0 if p <= 5]
+    assert not c[2].any()
+    assert c[3].all()
+    assert np.all(np.isneginf(s[c == 0])) and np.all(np.isfinite(s[c == 1]))
+
+
+def test_index_scores_row_uses_its_sequence():
+    rng = np.random.default_rng(25)
+    q, w, keys = _score_case(rng, 1, 2, 8, 2, 8)
+    ids, nv = _all_valid(2, 8)
+    pos = np.full(1, 10 ** 6, np.int32)
+    a, _ = oracle.index_scores(q, w, np.array([1], np.int32), pos, keys, ids, nv, kpool=4,
+                               first_key=0, scale=0.125)
+    b, _ = oracle.index_scores(q, w, np.array([0], np.int32), pos, keys[::-1].copy(), ids, nv,
+                               kpool=4, first_key=0, scale=0.125)
+    assert np.array_equal(a, b)
+
+
+def test_index_scores_fp8_keys_equal_decoded_bf16_keys():
+    rng = np.random.default_rng(26)
+    Q, B, P, Hi, D = 2, 2, 9, 3, 16
+    q, w, _ = _score_case(rng, Q, B, P, Hi, D)
+    kv = rng.integers(-8, 9, (B, P, D)) / 8.0
+    codes = synth.e4m3_codes(kv)
+    sc = np.exp2(rng.integers(-3, 3, (B, P))).astype(np.float32)
+    as_bf16 = synth.bf16_bits((kv * sc[..., None]).astype(np.float32))
+    ids, nv = _all_valid(B, P)
+    seq = np.array([0, 1], np.int32)
+    pos = np.full(Q, 10 ** 6, np.int32)
+    a, _ = oracle.index_scores(q, w, seq, pos, codes, ids, nv, kpool=8, first_key=0, scale=0.125,
+                               key_scales=sc)
+    b, _ = oracle.index_scores(q, w, seq, pos, as_bf16, ids, nv, kpool=8, first_key=0, scale=0.125)
+    assert np.array_equal(a, b)
+
+
+def test_index_scores_negative_zero_is_canonical():
+    q = np.zeros((1, 2, 4), np.uint16)
+    keys = np.zeros((1, 3, 4), np.uint16)
+    w = np.array([[-1.0, -2.0]], np.float32)
+    ids, nv = _all_valid(1, 3)
+    s, _ = oracle.index_scores(q, w, np.zeros(1, np.int32), np.full(1, 99, np.int32), keys, ids,
+                               nv, kpool=4, first_key=0, scale=1.0)
+    assert np.all(s == 0) and not np.any(np.signbit(s))
+
+
+# ------------------------------------------------------------------ topk_pools
+
+def _rank_select(score, cand, kw):
+    """Selection by the rank definition: p is chosen iff fewer than kw candidates beat it,
+    where q beats p if its score is higher, or equal with a lower pool index."""
+    P = len(score)
+    chosen = []
+    for p in range(P):
+        if not cand[p]:
+            continue
+        beat = sum(1 for o in range(P) if cand[o] and (score[o] > score[p] or
+                                                        (score[o] == score[p] and o < p)))
+        if beat < kw:
+            chosen.append(p)
+    return chosen + [-1] * (kw - len(chosen))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_rank_definition(seed):
+    rng = np.random.default_rng(100 + seed)
+    Q, P, kw = 4, 40, 7
+    scores = (rng.integers(-5, 6, (Q, P)) / 2.0).astype(np.float32)   # many ties
+    cand = (rng.random((Q, P)) > 0.3).astype(np.uint8)
+    cand[0, :] = 0
+    cand[0, [3, 9]] = 1                                                 # fewer than kw
+    scores[cand == 0] = -np.inf
+    sel = oracle.topk_pools(scores, cand, kw)
+    for r in range(Q):
+        assert list(sel[r]) == _rank_select(scores[r], cand[r], kw), r
+
+
+def test_topk_all_equal_takes_lowest_ids_and_zero_signs_tie():
+    P, kw = 30, 5
+    scores = np.zeros((2, P), np.float32)
+    scores[1, ::2] = -0.0
+    cand = np.ones((2, P), np.uint8)
+    sel = oracle.topk_pools(scores, cand, kw)
+    assert list(sel[0]) == [0, 1, 2, 3, 4]
+    assert list(sel[1]) == [0, 1, 2, 3, 4]
+    neg = np.array([[-1.0, -3.0, -2.0, -0.5]], np.float32)
+    assert list(oracle.topk_pools(neg, np.ones((1, 4), np.uint8), 2)[0]) == [0, 3]
+
+
+# ------------------------------------------------------------------ expand_selection
+
+@pytest.mark.parametrize("KP,f,tail", [(4, 0, False), (4, 0, True), (8, 3, True), (2, 1, True)])
+def test_expand_every_slot_explained(KP, f, tail):
+    rng = np.random.default_rng(KP + f)
+    S, T = 200, 8 * KP
+    kw = T // KP
+    P = (S - f) // KP
+    Q = 6
+    sel = np.full((Q, kw), -1, np.int32)
+    for r in range(Q):
+        n = int(rng.integers(0, kw + 1))
+        sel[r, :n] = np.sort(rng.choice(P, n, replace=False))
+    valid = (rng.random((1, S)) > 0.2).astype(np.uint8)
+    row_seq = np.zeros(Q, np.int32)
+    row_pos = np.array([f - 1, f, f + KP - 1, f + KP, 150, S - 1], np.int32)
+    tok = oracle.expand_selection(sel, row_seq, row_pos, valid, kpool=KP, index_topk=T,
+                                  always_select_tail=tail, first_key=f)
+    W = T + (KP - 1 if tail else 0)
+    assert tok.shape == (Q, W)
+    for r in range(Q):
+        pools = [p for p in sel[r] if p >= 0]
+        body = sorted(t for p in pools for t in range(f + p * KP, f + (p + 1) * KP))
+        assert [t for t in tok[r, :T] if t >= 0] == body
+        assert np.all(tok[r, len(pools) * KP:T] == -1)
+        if tail:
+            pos = row_pos[r]
+            n_tail = (pos + 1 - f) % KP if pos + 1 > f else 0
+            start = pos + 1 - n_tail
+            want = [t if valid[0, t] else -1 for t in range(start, pos + 1)]
+            assert list(tok[r, T:T + n_tail]) == want
+            assert np.all(tok[r, T + n_tail:] == -1)
+
+
+# ------------------------------------------------------------------ sparse MLA decode
+
+def _mla_case(rng, Q, H, C, B, S, W):
+    q = synth.bf16_bits(rng.standard_normal((Q, H, C)).astype(np.float32) * 0.5)
+    kv = synth.bf16_bits(rng.standard_normal((B * S, C)).astype(np.float32) * 0.5)
+    tok = np.stack([np.sort(rng.choice(S, W, replace=False)) for _ in range(Q)]).astype(np.int32)
+    seq = rng.integers(0, B, Q).astype(np.int32)
+    return q, kv, tok, seq
+
+
+def test_mla_single_token_copies_its_row_and_lse_is_logit():
+    rng = np.random.default_rng(31)
+    Q, H, C, B, S = 3, 2, 64, 2, 20
+    q, kv, _, seq = _mla_case(rng, Q, H, C, B, S, 1)
+    tok = np.full((Q, 5), -1, np.int32)
+    tok[:, 2] = [4, 7, 19]
+    out, lse = oracle.sparse_mla(q, tok, seq, kv, sm_scale=0.0625, S=S)
+    kvf = synth.bf16_to_f32(kv).astype(np.float64)
+    qf = synth.bf16_to_f32(q).astype(np.float64)
+    for r in range(Q):
+        row = kvf[seq[r] * S + tok[r, 2]]
+        for h in range(H):
+            assert np.array_equal(out[r, h], row.astype(np.float32))
+            assert np.isclose(lse[r, h], 0.0625 * qf[r, h] @ row, rtol=1e-6, atol=1e-6)
+
+
+def test_mla_zero_query_is_mean_of_rows():
+    rng = np.random.default_rng(32)
+    Q, H, C, B, S, W = 2, 3, 32, 1, 50, 9
+    _, kv, tok, seq = _mla_case(rng, Q, H, C, B, S, W)
+    q = np.zeros((Q, H, C), np.uint16)
+    out, lse = oracle.sparse_mla(q, tok, seq, kv, sm_scale=0.0625, S=S)
+    kvf = synth.bf16_to_f32(kv).astype(np.float64)
+    for r in range(Q):
+        want = kvf[tok[r]].mean(axis=0)
+        assert np.allclose(out[r], want[None], rtol=1e-6, atol=1e-7)
+        assert np.allclose(lse[r], math.log(W))
+
+
+def test_mla_sparse_with_every_token_equals_dense_sdpa():
+    """Selecting every valid token reduces sparse attention to dense attention, here computed
+    by torch's scaled_dot_product_attention in float64 on the CPU."""
+    rng = np.random.default_rng(33)
+    Q, H, C, S = 2, 4, 128, 40
+    q, kv, _, _ = _mla_case(rng, Q, H, C, 1, S, 1)
+    L = [29, 40]
+    tok = np.full((Q, 48), -1, np.int32)
+    for r in range(Q):
+        tok[r, :L[r]] = np.arange(L[r])
+    seq = np.zeros(Q, np.int32)
+    out, _ = oracle.sparse_mla(q, tok, seq, kv, sm_scale=0.0625, S=S)
+    qt = torch.from_numpy(synth.bf16_to_f32(q).astype(np.float64))
+    kt = torch.from_numpy(synth.bf16_to_f32(kv).astype(np.float64))
+    for r in range(Q):
+        k = kt[:L[r]]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt[r][None, None], k[None, None].expand(1, 1, -1, -1), k[None, None],
+            scale=0.0625)[0, 0]
+        assert np.allclose(out[r], ref.numpy(), rtol=1e-6, atol=1e-7)
+
+
+def test_mla_masked_slots_and_paging_do_not_change_the_result():
+    rng = np.random.default_rng(34)
+    Q, H, C, B, S, W = 3, 2, 64, 2, 128, 12
+    q, kv, tok, seq = _mla_case(rng, Q, H, C, B, S, W)
+    out, lse = oracle.sparse_mla(q, tok, seq, kv, sm_scale=0.0625, S=S)
+    # interleave -1 slots: same tokens in the same order
+    holes = np.full((Q, 2 * W + 3), -1, np.int32)
+    holes[:, 1:2 * W:2] = tok
+    out2, lse2 = oracle.sparse_mla(q, holes, seq, kv, sm_scale=0.0625, S=S)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    # the same rows scattered into shuffled 16-token blocks
+    bs = 16
+    nblk = B * S // bs
+    perm = rng.permutation(nblk).astype(np.int32)
+    table = perm.reshape(B, S // bs)
+    paged = np.zeros_like(kv)
+    for b in range(B):
+        for j in range(S // bs):
+            paged[table[b, j] * bs:(table[b, j] + 1) * bs] = kv[b * S + j * bs:b * S + (j + 1) * bs]
+    out3, lse3 = oracle.sparse_mla(q, tok, seq, paged, sm_scale=0.0625, block_table=table,
+                                   block_size=bs)
+    assert np.array_equal(out, out3) and np.array_equal(lse, lse3)
+
+
+def test_mla_fp8_latent_equals_decoded_bf16_latent_and_empty_row():
+    rng = np.random.default_rng(35)
+    Q, H, C, B, S, W = 2, 2, 32, 1, 30, 6
+    q, _, tok, seq = _mla_case(rng, Q, H, C, B, S, W)
+    vals = rng.integers(-8, 9, (S, C)) / 8.0
+    codes = synth.e4m3_codes(vals)
+    sc = np.exp2(rng.integers(-2, 2, S)).astype(np.float32)
+    as_bf16 = synth.bf16_bits((vals * sc[:, None]).astype(np.float32))
+    a, la = oracle.sparse_mla(q, tok, seq, codes, sm_scale=0.0625, S=S, kv_scales=sc)
+    b, lb = oracle.sparse_mla(q, tok, seq, as_bf16, sm_scale=0.0625, S=S)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    empty = np.full((1, 4), -1, np.int32)
+    o, l = oracle.sparse_mla(q[:1], empty, seq[:1], as_bf16, sm_scale=0.0625, S=S)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
+# ------------------------------------------------------------------ absorb transforms
+
+def _absorb_dims():
+    return dict(heads=3, nope=8, vd=6, kvl=16, ql=10, hidden=12)
+
+
+def test_absorb_identity_blocks():
+    d = _absorb_dims()
+    H, nope, vd, kvl, ql = d["heads"], d["nope"], d["vd"], d["kvl"], d["ql"]
+    rng = np.random.default_rng(41)
+    q_b = rng.standard_normal((H * nope, ql)).astype(np.float32)
+    # K half of head h = [I_nope | 0]: q_absorb row h*kvl + c is q_b row h*nope + c for c < nope
+    kv_b = np.zeros((H * (nope + vd), kvl), np.float32)
+    for h in range(H):
+        kv_b[h * (nope + vd):h * (nope + vd) + nope, :nope] = np.eye(nope)
+        kv_b[h * (nope + vd) + nope:(h + 1) * (nope + vd)] = rng.standard_normal((vd, kvl))
+    qa = oracle.absorb_q(q_b, kv_b, heads=H, nope=nope, rope=0, vd=vd, kvl=kvl, ql=ql)
+    for h in range(H):
+        assert np.array_equal(qa[h * kvl:h * kvl + nope], q_b[h * nope:(h + 1) * nope])
+        assert np.all(qa[h * kvl + nope:(h + 1) * kvl] == 0)
+    # V half of head h = [I_vd | 0]: o_absorb columns h*kvl + c equal o_proj columns h*vd + c
+    kv_v = np.zeros_like(kv_b)
+    for h in range(H):
+        kv_v[h * (nope + vd) + nope:(h + 1) * (nope + vd), :vd] = np.eye(vd)
+    o = rng.standard_normal((d["hidden"], H * vd)).astype(np.float32)
+    oa = oracle.absorb_o(o, kv_v, heads=H, nope=nope, rope=0, vd=vd, kvl=kvl, hidden=d["hidden"])
+    for h in range(H):
+        assert np.array_equal(oa[:, h * kvl:h * kvl + vd], o[:, h * vd:(h + 1) * vd])
+        assert np.all(oa[:, h * kvl + vd:(h + 1) * kvl] == 0)
+
+
+def test_absorb_equals_multi_head_attention():
+    """The absorbed form is the textbook MLA identity: attention over the shared latent with
+    absorbed q and o equals multi-head attention with q = W_UQ c_q, k = W_UK c, v = W_UV c."""
+    d = _absorb_dims()
+    H, nope, vd, kvl, ql, hid = d["heads"], d["nope"], d["vd"], d["kvl"], d["ql"], d["hidden"]
+    rng = np.random.default_rng(42)
+    q_b = rng.standard_normal((H * nope, ql)).astype(np.float32) * 0.3
+    kv_b = rng.standard_normal((H * (nope + vd), kvl)).astype(np.float32) * 0.3
+    o = rng.standard_normal((hid, H * vd)).astype(np.float32) * 0.3
+    qa = oracle.absorb_q(q_b, kv_b, heads=H, nope=nope, rope=0, vd=vd, kvl=kvl, ql=ql)
+    oa = oracle.absorb_o(o, kv_b, heads=H, nope=nope, rope=0, vd=vd, kvl=kvl, hidden=hid)
+    cq = rng.standard_normal(ql)
+    lat = rng.standard_normal((7, kvl))
+    sm = 0.25
+    # multi-head attention in f64
+    y = np.zeros(hid)
+    for h in range(H):
+        Wuq = q_b[h * nope:(h + 1) * nope].astype(np.float64)
+        Wuk = kv_b[h * (nope + vd):h * (nope + vd) + nope].astype(np.float64)
+        Wuv = kv_b[h * (nope + vd) + nope:(h + 1) * (nope + vd)].astype(np.float64)
+        qh, kh, vh = Wuq @ cq, lat @ Wuk.T, lat @ Wuv.T
+        a = np.exp(sm * kh @ qh - np.max(sm * kh @ qh))
+        a /= a.sum()
+        y += o[:, h * vd:(h + 1) * vd].astype(np.float64) @ (a @ vh)
+    # absorbed form
+    z = np.zeros(hid)
+    for h in range(H):
+        qlat = qa[h * kvl:(h + 1) * kvl].astype(np.float64) @ cq
+        a = np.exp(sm * lat @ qlat - np.max(sm * lat @ qlat))
+        a /= a.sum()
+        z += oa[:, h * kvl:(h + 1) * kvl].astype(np.float64) @ (a @ lat)
+    assert np.allclose(y, z, rtol=1e-5, atol=1e-5)
+
+
+def test_absorb_refusals():
+    d = _absorb_dims()
+    H, nope, vd, kvl, ql, hid = d["heads"], d["nope"], d["vd"], d["kvl"], d["ql"], d["hidden"]
+    q_b = np.zeros(H * nope * ql, np.float32)
+    kv_b = np.zeros(H * (nope + vd) * kvl, np.float32)
+    o = np.zeros(hid * H * vd, np.float32)
+    with pytest.raises(oracle.OracleRefusal) as e:
+        oracle.absorb_q(q_b[:-1], kv_b, heads=H, nope=nope, rope=0, vd=vd, kvl=kvl, ql=ql)
+    assert e.value.code == 1
+    with pytest.raises(oracle.OracleRefusal) as e:
+        oracle.absorb_q(q_b, kv_b[1:], heads=H, nope=nope, rope=0, vd=vd, kvl=kvl, ql=ql)
+    assert e.value.code == 2
+    qr = np.zeros(H * (nope + 2) * ql, np.float32)
+    with pytest.raises(oracle.OracleRefusal) as e:
+        oracle.absorb_q(qr, kv_b, heads=H, nope=nope, rope=2, vd=vd, kvl=kvl, ql=ql)
+    assert e.value.code == 3
+    with pytest.raises(oracle.OracleRefusal) as e:
+        oracle.absorb_o(o, kv_b, heads=H, nope=nope, rope=1, vd=vd, kvl=kvl, hidden=hid)
+    assert e.value.code == 3
+    with pytest.raises(oracle.OracleRefusal) as e:
+        oracle.absorb_o(o[1:], kv_b, heads=H, nope=nope, rope=0, vd=vd, kvl=kvl, hidden=hid)
+    assert e.value.code == 1
+    with pytest.raises(oracle.OracleRefusal) as e:
+        oracle.absorb_o(o, kv_b[1:], heads=H, nope=nope, rope=0, vd=vd, kvl=kvl, hidden=hid)
+    assert e.value.code == 2
+
+
+# ------------------------------------------------------------------ end to end on a tiny case
+
+def test_tiny_chain_selects_the_pools_a_brute_force_ranking_picks():
+    """The oracle chain on the tiny workload: the selected pools are the rank-definition
+    top-k of the f64 scores computed here directly from the drawn arrays."""
+    di = synth.make_decode_inputs("tiny")
+    wl = di.wl
+    ids, nv = oracle.compact_pools(di.pool_valid)
+    sc, cd = oracle.index_scores(di.q, di.w, di.row_seq, di.row_pos, di.keys, ids, nv,
+                                 kpool=wl.kpool, first_key=wl.first_key, scale=di.scale)
+    assert cd.sum() == 255 and not cd[0, 255]
+    qf = synth.bf16_to_f32(di.q)[0].astype(np.float64)
+    kf = synth.bf16_to_f32(di.keys)[0].astype(np.float64)
+    ref = (di.w[0].astype(np.float64)[:, None] *
+           np.maximum(di.scale * qf @ kf.T, 0)).sum(0)
+    assert np.allclose(sc[0, :255], ref[:255], rtol=1e-6, atol=1e-6)
+    sel = oracle.topk_pools(sc, cd, wl.kw)
+    assert list(sel[0]) == _rank_select(sc[0], cd[0], wl.kw)
