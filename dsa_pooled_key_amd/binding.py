@@ -1,0 +1,368 @@
+"""ctypes binding of libdsa (include/dsa.h): argument marshalling only.
+
+Every function here checks tensor devices, dtypes, shapes and contiguity, allocates outputs
+that were not passed in (plain torch allocations on the input's device), and calls the C
+entry point of the same name on the current torch stream. All arithmetic happens in the HIP
+kernels; there is no fallback path. Loading fails loudly when libdsa.so has not been built.
+
+Tensor conventions: bf16 data is ``torch.bfloat16``; fp8 data is OCP e4m3 passed as
+``torch.float8_e4m3fn`` or as its raw ``torch.uint8`` codes; ids are ``torch.int32``; masks
+are ``torch.uint8``.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdsa.so")
+
+DSA_BF16, DSA_F32, DSA_FP8_E4M3 = 0, 1, 2
+ERROR_NAMES = {
+    -1: "DSA_ERR_NULL_ARG", -2: "DSA_ERR_BAD_SIZE", -3: "DSA_ERR_BAD_DTYPE",
+    -4: "DSA_ERR_KPOOL_OR_TOPK_ZERO", -5: "DSA_ERR_TOPK_NOT_MULTIPLE", -6: "DSA_ERR_KPOOL_GT_MAX",
+    -7: "DSA_ERR_KV_LORA_ZERO", -8: "DSA_ERR_KV_LORA_NOT_512", -9: "DSA_ERR_ZERO_HEADS",
+    -10: "DSA_ERR_ROPE_UNSUPPORTED", -11: "DSA_ERR_ELEM_COUNT", -12: "DSA_ERR_WORKSPACE",
+    -13: "DSA_ERR_HIP", -14: "DSA_ERR_UNSUPPORTED",
+}
+EXPORTED = [
+    "dsa_last_error", "dsa_version", "dsa_config_validate", "dsa_select_k", "dsa_out_width",
+    "dsa_num_pools", "dsa_kpool_compress", "dsa_compact_pools", "dsa_index_scores",
+    "dsa_topk_pools", "dsa_expand_selection", "dsa_sparse_mla_decode_workspace",
+    "dsa_sparse_mla_decode", "dsa_absorb_q", "dsa_absorb_o", "dsa_f32_to_bf16_rne",
+]
+
+
+class DsaError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERROR_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    """dsa_config: per-layer geometry (mod.rs, Glm5NextDsaConfig)."""
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "index_heads", "index_head_dim", "index_kpool", "index_topk", "always_select_tail",
+        "heads", "kv_lora_rank", "qk_nope_head_dim", "qk_rope_head_dim", "v_head_dim",
+        "q_lora_rank", "hidden")]
+
+    @classmethod
+    def make(cls, *, index_heads, index_head_dim, index_kpool, index_topk, heads,
+             always_select_tail=False, kv_lora_rank=512, qk_nope_head_dim=256,
+             qk_rope_head_dim=0, v_head_dim=256, q_lora_rank=0, hidden=0):
+        return cls(index_heads, index_head_dim, index_kpool, index_topk, int(always_select_tail),
+                   heads, kv_lora_rank, qk_nope_head_dim, qk_rope_head_dim, v_head_dim,
+                   q_lora_rank, hidden)
+
+
+_lib = None
+_P, _I, _I64, _SZ, _F = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
+                         ctypes.c_float)
+_CFG = ctypes.POINTER(Config)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "dsa_last_error": ([], ctypes.c_char_p),
+            "dsa_version": ([], ctypes.c_char_p),
+            "dsa_config_validate": ([_CFG], _I),
+            "dsa_select_k": ([_CFG, _I64], _I64),
+            "dsa_out_width": ([_CFG], _I64),
+            "dsa_num_pools": ([_I64, _I64, _I64], _I64),
+            "dsa_kpool_compress": ([_CFG, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P], _I),
+            "dsa_compact_pools": ([_I, _I, _P, _P, _P, _P], _I),
+            "dsa_index_scores": ([_CFG, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P, _P, _P,
+                                  _P, _P, _P], _I),
+            "dsa_topk_pools": ([_CFG, _I, _I, _P, _P, _P, _P], _I),
+            "dsa_expand_selection": ([_CFG, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P], _I),
+            "dsa_sparse_mla_decode_workspace": ([_CFG, _I, _I], _SZ),
+            "dsa_sparse_mla_decode": ([_CFG, _I, _I, _I, _F, _P, _P, _P, _P, _I, _P, _I64, _I,
+                                       _P, _I, _I, _P, _P, _P, _SZ, _P], _I),
+            "dsa_absorb_q": ([_CFG, _P, _SZ, _P, _SZ, _I, _I, _P, _SZ], _I),
+            "dsa_absorb_o": ([_CFG, _P, _SZ, _P, _SZ, _I, _I, _P, _SZ], _I),
+            "dsa_f32_to_bf16_rne": ([_P, _P, _SZ], None),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().dsa_last_error().decode()
+
+
+def version() -> str:
+    return lib().dsa_version().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise DsaError(rc, last_error())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtypes, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must live on the GPU")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    return t
+
+
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype in _FP8:
+        return DSA_FP8_E4M3
+    raise TypeError(f"unsupported data dtype {t.dtype}")
+
+
+# ------------------------------------------------------------------ geometry
+
+def config_validate(cfg: Config) -> int:
+    return int(lib().dsa_config_validate(ctypes.byref(cfg)))
+
+
+def select_k(cfg: Config, n_pools: int) -> int:
+    v = int(lib().dsa_select_k(ctypes.byref(cfg), n_pools))
+    _check(min(v, 0))
+    return v
+
+
+def out_width(cfg: Config) -> int:
+    v = int(lib().dsa_out_width(ctypes.byref(cfg)))
+    _check(min(v, 0))
+    return v
+
+
+def num_pools(S: int, first_key: int, kpool: int) -> int:
+    v = int(lib().dsa_num_pools(S, first_key, kpool))
+    _check(min(v, 0))
+    return v
+
+
+# ------------------------------------------------------------------ the six steps
+
+def kpool_compress(cfg: Config, k, gate, ape, valid, first_key: int = 0, pool_keys=None,
+                   pool_valid=None):
+    """k, gate [B,S,D] bf16; ape [KP,D] f32; valid [B,S] u8 -> (pool_keys [B,P,D] bf16,
+    pool_valid [B,P] u8)."""
+    _dev(k, "k", (torch.bfloat16,))
+    B, S, D = k.shape
+    KP = cfg.index_kpool
+    _dev(gate, "gate", (torch.bfloat16,), (B, S, D))
+    _dev(ape, "ape", (torch.float32,), (KP, D))
+    _dev(valid, "valid", (torch.uint8,), (B, S))
+    if D != cfg.index_head_dim:
+        raise ValueError("key width differs from index_head_dim")
+    P = num_pools(S, first_key, KP)
+    if pool_keys is None:
+        pool_keys = torch.empty((B, P, D), dtype=torch.bfloat16, device=k.device)
+    if pool_valid is None:
+        pool_valid = torch.empty((B, P), dtype=torch.uint8, device=k.device)
+    _dev(pool_keys, "pool_keys", (torch.bfloat16,), (B, P, D))
+    _dev(pool_valid, "pool_valid", (torch.uint8,), (B, P))
+    _check(lib().dsa_kpool_compress(ctypes.byref(cfg), B, S, first_key, _ptr(k), _ptr(gate),
+                                    _ptr(ape), _ptr(valid), _ptr(pool_keys), _ptr(pool_valid),
+                                    _stream(k)))
+    return pool_keys, pool_valid
+
+
+def compact_pools(pool_valid, ids=None, n_valid=None):
+    """pool_valid [B,P] u8 -> (ids [B,P] i32, n_valid [B] i32)."""
+    _dev(pool_valid, "pool_valid", (torch.uint8,))
+    B, P = pool_valid.shape
+    if ids is None:
+        ids = torch.empty((B, P), dtype=torch.int32, device=pool_valid.device)
+    if n_valid is None:
+        n_valid = torch.empty((B,), dtype=torch.int32, device=pool_valid.device)
+    _dev(ids, "ids", (torch.int32,), (B, P))
+    _dev(n_valid, "n_valid", (torch.int32,), (B,))
+    _check(lib().dsa_compact_pools(B, P, _ptr(pool_valid), _ptr(ids), _ptr(n_valid),
+                                   _stream(pool_valid)))
+    return ids, n_valid
+
+
+def index_scores(cfg: Config, q, w, row_seq, row_pos, keys, ids, n_valid, *, first_key: int,
+                 scale: float, key_scales=None, scores=None, cand=None):
+    """q [Q,Hi,D] bf16; w [Q,Hi] f32; keys [B,P,D] bf16 or fp8 (+ key_scales [B,P] f32)
+    -> (scores [Q,P] f32, cand [Q,P] u8)."""
+    _dev(q, "q", (torch.bfloat16,))
+    Q, Hi, D = q.shape
+    _dev(w, "w", (torch.float32,), (Q, Hi))
+    _dev(row_seq, "row_seq", (torch.int32,), (Q,))
+    _dev(row_pos, "row_pos", (torch.int32,), (Q,))
+    _dev(keys, "keys", (torch.bfloat16,) + _FP8)
+    B, P, Dk = keys.shape
+    if Dk != D or D != cfg.index_head_dim or Hi != cfg.index_heads:
+        raise ValueError("q / keys shapes differ from the config's indexer geometry")
+    code = _dtype_code(keys)
+    if code == DSA_FP8_E4M3:
+        _dev(key_scales, "key_scales", (torch.float32,), (B, P))
+    _dev(ids, "ids", (torch.int32,), (B, P))
+    _dev(n_valid, "n_valid", (torch.int32,), (B,))
+    if scores is None:
+        scores = torch.empty((Q, P), dtype=torch.float32, device=q.device)
+    if cand is None:
+        cand = torch.empty((Q, P), dtype=torch.uint8, device=q.device)
+    _dev(scores, "scores", (torch.float32,), (Q, P))
+    _dev(cand, "cand", (torch.uint8,), (Q, P))
+    _check(lib().dsa_index_scores(ctypes.byref(cfg), Q, B, P, first_key, float(scale), _ptr(q),
+                                  _ptr(w), _ptr(row_seq), _ptr(row_pos), _ptr(keys), code,
+                                  _ptr(key_scales) if code == DSA_FP8_E4M3 else None, _ptr(ids),
+                                  _ptr(n_valid), _ptr(scores), _ptr(cand), _stream(q)))
+    return scores, cand
+
+
+def topk_pools(cfg: Config, scores, cand, sel=None):
+    """scores [Q,P] f32, cand [Q,P] u8 -> sel [Q, select_k(P)] i32 (ascending, -1 padded)."""
+    _dev(scores, "scores", (torch.float32,))
+    Q, P = scores.shape
+    _dev(cand, "cand", (torch.uint8,), (Q, P))
+    kw = select_k(cfg, P)
+    if sel is None:
+        sel = torch.empty((Q, kw), dtype=torch.int32, device=scores.device)
+    _dev(sel, "sel", (torch.int32,), (Q, kw))
+    _check(lib().dsa_topk_pools(ctypes.byref(cfg), Q, P, _ptr(scores), _ptr(cand), _ptr(sel),
+                                _stream(scores)))
+    return sel
+
+
+def expand_selection(cfg: Config, sel, row_seq, row_pos, valid, *, S: int, first_key: int,
+                     token_ids=None):
+    """sel [Q,Kw] i32 -> token_ids [Q, out_width] i32. valid [B,S] u8 (read for the tail)."""
+    _dev(sel, "sel", (torch.int32,))
+    Q, kw = sel.shape
+    _dev(row_seq, "row_seq", (torch.int32,), (Q,))
+    _dev(row_pos, "row_pos", (torch.int32,), (Q,))
+    _dev(valid, "valid", (torch.uint8,))
+    B = valid.shape[0]
+    if valid.shape[1] != S:
+        raise ValueError("valid must be [B, S]")
+    W = out_width(cfg)
+    if token_ids is None:
+        token_ids = torch.empty((Q, W), dtype=torch.int32, device=sel.device)
+    _dev(token_ids, "token_ids", (torch.int32,), (Q, W))
+    _check(lib().dsa_expand_selection(ctypes.byref(cfg), Q, kw, B, S, first_key, _ptr(sel),
+                                      _ptr(row_seq), _ptr(row_pos), _ptr(valid), _ptr(token_ids),
+                                      _stream(sel)))
+    return token_ids
+
+
+def sparse_mla_workspace(cfg: Config, Q: int, W: int) -> int:
+    return int(lib().dsa_sparse_mla_decode_workspace(ctypes.byref(cfg), Q, W))
+
+
+def sparse_mla_decode(cfg: Config, q_abs, token_ids, row_seq, kv, *, B: int, sm_scale: float,
+                      S: int = 0, kv_scales=None, block_table=None, block_size: int = 64,
+                      out=None, lse=None, ws=None):
+    """q_abs [Q,H,512] bf16; token_ids [Q,W] i32; kv [rows,512] bf16 or fp8 (+ kv_scales
+    [rows] f32); contiguous rows b*S + t, or paged through block_table [B, max_blocks].
+    Returns (out [Q,H,512] f32, lse [Q,H] f32)."""
+    _dev(q_abs, "q_abs", (torch.bfloat16,))
+    Q, H, C = q_abs.shape
+    if H != cfg.heads or C != 512:
+        raise ValueError("q_abs must be [Q, heads, 512]")
+    _dev(token_ids, "token_ids", (torch.int32,))
+    if token_ids.shape[0] != Q:
+        raise ValueError("token_ids rows differ from q_abs rows")
+    W = token_ids.shape[1]
+    _dev(row_seq, "row_seq", (torch.int32,), (Q,))
+    _dev(kv, "kv", (torch.bfloat16,) + _FP8)
+    if kv.shape[-1] != 512:
+        raise ValueError("kv rows must be 512 wide")
+    rows = kv.numel() // 512
+    code = _dtype_code(kv)
+    if code == DSA_FP8_E4M3:
+        _dev(kv_scales, "kv_scales", (torch.float32,))
+        if kv_scales.numel() != rows:
+            raise ValueError("kv_scales must hold one scale per latent row")
+    max_blocks = 0
+    if block_table is not None:
+        _dev(block_table, "block_table", (torch.int32,))
+        if block_table.shape[0] != B:
+            raise ValueError("block_table must be [B, max_blocks]")
+        max_blocks = block_table.shape[1]
+    if out is None:
+        out = torch.empty((Q, H, 512), dtype=torch.float32, device=q_abs.device)
+    if lse is None:
+        lse = torch.empty((Q, H), dtype=torch.float32, device=q_abs.device)
+    _dev(out, "out", (torch.float32,), (Q, H, 512))
+    _dev(lse, "lse", (torch.float32,), (Q, H))
+    need = sparse_mla_workspace(cfg, Q, W)
+    if need and ws is None:
+        ws = torch.empty((need,), dtype=torch.uint8, device=q_abs.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().dsa_sparse_mla_decode(ctypes.byref(cfg), Q, W, B, float(sm_scale), _ptr(q_abs),
+                                       _ptr(token_ids), _ptr(row_seq), _ptr(kv), code,
+                                       _ptr(kv_scales) if code == DSA_FP8_E4M3 else None, rows,
+                                       S, _ptr(block_table), max_blocks, block_size, _ptr(out),
+                                       _ptr(lse), _ptr(ws), ws_bytes, _stream(q_abs)))
+    return out, lse
+
+
+# ------------------------------------------------------------------ host weight prep
+
+def _host_f32(a, name):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def absorb_q(cfg: Config, q_b, kv_b, *, full_heads: int, threads: int = 0) -> np.ndarray:
+    """Host f32 (numpy) -> q_absorb [full_heads*kv_lora_rank, q_lora_rank]."""
+    q_b, pq = _host_f32(q_b, "q_b")
+    kv_b, pk = _host_f32(kv_b, "kv_b")
+    n = full_heads * cfg.kv_lora_rank * cfg.q_lora_rank
+    out = np.zeros(max(n, 1), np.float32)
+    _check(lib().dsa_absorb_q(ctypes.byref(cfg), pq, q_b.size, pk, kv_b.size, full_heads, threads,
+                              out.ctypes.data_as(ctypes.c_void_p), n))
+    return out[:n].reshape(full_heads * cfg.kv_lora_rank, cfg.q_lora_rank)
+
+
+def absorb_o(cfg: Config, o_local, kv_b_local, *, local_heads: int, threads: int = 0) -> np.ndarray:
+    """Host f32 (numpy) -> o_absorb [hidden, local_heads*kv_lora_rank]."""
+    o_local, po = _host_f32(o_local, "o_local")
+    kv_b_local, pk = _host_f32(kv_b_local, "kv_b_local")
+    n = cfg.hidden * local_heads * cfg.kv_lora_rank
+    out = np.zeros(max(n, 1), np.float32)
+    _check(lib().dsa_absorb_o(ctypes.byref(cfg), po, o_local.size, pk, kv_b_local.size,
+                              local_heads, threads, out.ctypes.data_as(ctypes.c_void_p), n))
+    return out[:n].reshape(cfg.hidden, local_heads * cfg.kv_lora_rank)
+
+
+def f32_to_bf16_rne(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros(x.shape, np.uint16)
+    lib().dsa_f32_to_bf16_rne(x.ctypes.data_as(ctypes.c_void_p),
+                              out.ctypes.data_as(ctypes.c_void_p), x.size)
+    return out

@@ -1,0 +1,274 @@
+// dsa_api.cpp -- the extern "C" entry points of libdsa declared in include/dsa.h.
+//
+// Every call checks its arguments on the host first (null pointers, sizes, alignment,
+// the config rules of mod.rs Glm5NextDsaConfig::validate) and launches nothing on a refusal.
+// Kernels are enqueued on the caller's stream; nothing here allocates or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "dsa.h"
+#include "dsa_host.hpp"
+#include "dsa_launch.hpp"
+
+namespace {
+thread_local char g_err[512] = "";
+}  // namespace
+
+namespace dsa_host {
+int set_error(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+void clear_error() { g_err[0] = 0; }
+}  // namespace dsa_host
+
+namespace {
+
+using dsa_host::clear_error;
+using dsa_host::set_error;
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return DSA_OK;
+    return set_error(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// The six refusals of mod.rs Glm5NextDsaConfig::validate, in the page's order.
+int check_config(const dsa_config *c) {
+    if (!c) return set_error(DSA_ERR_NULL_ARG, "config is NULL");
+    if (c->index_kpool == 0 || c->index_topk == 0)
+        return set_error(DSA_ERR_KPOOL_OR_TOPK_ZERO,
+                    "index_kpool and index_topk must both be positive (got %d and %d)",
+                    c->index_kpool, c->index_topk);
+    if (c->index_kpool < 0 || c->index_topk < 0)
+        return set_error(DSA_ERR_BAD_SIZE, "index_kpool and index_topk must be positive");
+    if (c->index_topk % c->index_kpool != 0)
+        return set_error(DSA_ERR_TOPK_NOT_MULTIPLE,
+                    "index_topk %d is not a whole number of pools of %d tokens", c->index_topk,
+                    c->index_kpool);
+    if (c->index_kpool > DSA_MAX_KPOOL)
+        return set_error(DSA_ERR_KPOOL_GT_MAX,
+                    "index_kpool %d is above the %d pool slots the pooling kernel holds",
+                    c->index_kpool, DSA_MAX_KPOOL);
+    if (c->kv_lora_rank == 0) return set_error(DSA_ERR_KV_LORA_ZERO, "kv_lora_rank is 0; MLA needs a latent");
+    if (c->kv_lora_rank != DSA_LATENT_DIM)
+        return set_error(DSA_ERR_KV_LORA_NOT_512,
+                    "kv_lora_rank %d differs from the %d-wide latent the decode kernels read",
+                    c->kv_lora_rank, DSA_LATENT_DIM);
+    if (c->heads == 0) return set_error(DSA_ERR_ZERO_HEADS, "no attention heads on this device");
+    if (c->heads < 0) return set_error(DSA_ERR_BAD_SIZE, "heads is negative");
+    return DSA_OK;
+}
+
+int check_index_geometry(const dsa_config *c) {
+    if (c->index_heads <= 0 || c->index_heads > DSA_MAX_INDEX_HEADS)
+        return set_error(DSA_ERR_UNSUPPORTED, "index_heads %d outside 1..%d", c->index_heads,
+                    DSA_MAX_INDEX_HEADS);
+    if (c->index_head_dim != 32 && c->index_head_dim != 64 && c->index_head_dim != 128)
+        return set_error(DSA_ERR_UNSUPPORTED, "index_head_dim %d is not 32, 64 or 128",
+                    c->index_head_dim);
+    return DSA_OK;
+}
+
+int64_t num_pools(int64_t S, int64_t first_key, int64_t kpool) {
+    if (S <= first_key) return 0;
+    return (S - first_key) / kpool;
+}
+
+int64_t select_k(const dsa_config *c, int64_t n_pools) {
+    const int64_t k = c->index_topk / c->index_kpool;
+    return k < n_pools ? k : n_pools;
+}
+
+int64_t out_width(const dsa_config *c) {
+    return (int64_t)c->index_topk + (c->always_select_tail ? c->index_kpool - 1 : 0);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dsa_last_error(void) { return g_err; }
+
+const char *dsa_version(void) { return "dsa 0.1.0 gfx950"; }
+
+int dsa_config_validate(const dsa_config *cfg) {
+    clear_error();
+    return check_config(cfg);
+}
+
+int64_t dsa_select_k(const dsa_config *cfg, int64_t n_pools) {
+    clear_error();
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (n_pools < 0) return set_error(DSA_ERR_BAD_SIZE, "n_pools is negative");
+    return select_k(cfg, n_pools);
+}
+
+int64_t dsa_out_width(const dsa_config *cfg) {
+    clear_error();
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    return out_width(cfg);
+}
+
+int64_t dsa_num_pools(int64_t S, int64_t first_key, int64_t kpool) {
+    clear_error();
+    if (kpool <= 0 || S < 0 || first_key < 0)
+        return set_error(DSA_ERR_BAD_SIZE, "num_pools needs kpool > 0 and non-negative S, first_key");
+    return num_pools(S, first_key, kpool);
+}
+
+int dsa_kpool_compress(const dsa_config *cfg, int B, int S, int first_key, const void *k,
+                       const void *gate, const float *ape, const uint8_t *valid, void *pool_keys,
+                       uint8_t *pool_valid, hipStream_t stream) {
+    clear_error();
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    const int D = cfg->index_head_dim;
+    if (D <= 0 || D % 8 != 0 || D > 1024)
+        return set_error(DSA_ERR_UNSUPPORTED, "index_head_dim %d must be a positive multiple of 8", D);
+    if (B < 0 || S < 0 || first_key < 0) return set_error(DSA_ERR_BAD_SIZE, "negative B, S or first_key");
+    const int64_t P = num_pools(S, first_key, cfg->index_kpool);
+    if ((int64_t)B * P == 0) return DSA_OK;
+    if (!k || !gate || !ape || !valid || !pool_keys || !pool_valid)
+        return set_error(DSA_ERR_NULL_ARG, "kpool_compress: a buffer is NULL");
+    if (!aligned(k, 16) || !aligned(gate, 16) || !aligned(pool_keys, 16) || !aligned(ape, 16))
+        return set_error(DSA_ERR_BAD_SIZE, "kpool_compress: k, gate, pool_keys and ape need 16-byte alignment");
+    return hip_status(dsa::launch_kpool_compress(B, S, D, cfg->index_kpool, first_key, (int)P,
+                                                 static_cast<const uint16_t *>(k),
+                                                 static_cast<const uint16_t *>(gate), ape, valid,
+                                                 static_cast<uint16_t *>(pool_keys), pool_valid,
+                                                 stream),
+                      "kpool_compress launch");
+}
+
+int dsa_compact_pools(int B, int P, const uint8_t *pool_valid, int32_t *ids, int32_t *n_valid,
+                      hipStream_t stream) {
+    clear_error();
+    if (B < 0 || P < 0) return set_error(DSA_ERR_BAD_SIZE, "negative B or P");
+    if (B == 0) return DSA_OK;
+    if (!n_valid || (P > 0 && (!pool_valid || !ids)))
+        return set_error(DSA_ERR_NULL_ARG, "compact_pools: a buffer is NULL");
+    return hip_status(dsa::launch_compact_pools(B, P, pool_valid, ids, n_valid, stream),
+                      "compact_pools launch");
+}
+
+int dsa_index_scores(const dsa_config *cfg, int Q, int B, int P, int first_key, float scale,
+                     const void *q, const float *w, const int32_t *row_seq,
+                     const int32_t *row_pos, const void *keys, dsa_dtype key_dtype,
+                     const float *key_scales, const int32_t *ids, const int32_t *n_valid,
+                     float *scores, uint8_t *cand, hipStream_t stream) {
+    clear_error();
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_index_geometry(cfg))) return rc;
+    if (Q < 0 || B < 0 || P < 0 || first_key < 0) return set_error(DSA_ERR_BAD_SIZE, "negative size");
+    if (key_dtype != DSA_BF16 && key_dtype != DSA_FP8_E4M3)
+        return set_error(DSA_ERR_BAD_DTYPE, "index_scores: keys must be bf16 or fp8 e4m3");
+    if (Q == 0 || P == 0) return DSA_OK;
+    if (B == 0) return set_error(DSA_ERR_BAD_SIZE, "index_scores: rows need at least one sequence");
+    if (!q || !w || !row_seq || !row_pos || !keys || !ids || !n_valid || !scores || !cand)
+        return set_error(DSA_ERR_NULL_ARG, "index_scores: a buffer is NULL");
+    const bool fp8 = key_dtype == DSA_FP8_E4M3;
+    if (fp8 && !key_scales) return set_error(DSA_ERR_NULL_ARG, "index_scores: fp8 keys need key_scales");
+    if (!aligned(q, 16) || !aligned(keys, 16))
+        return set_error(DSA_ERR_BAD_SIZE, "index_scores: q and keys need 16-byte alignment");
+    if ((long long)first_key + (long long)P * cfg->index_kpool > 0x7fffffffLL)
+        return set_error(DSA_ERR_BAD_SIZE, "index_scores: token positions exceed int32");
+    return hip_status(dsa::launch_index_scores(Q, B, P, cfg->index_heads, cfg->index_head_dim,
+                                               cfg->index_kpool, first_key, scale,
+                                               static_cast<const uint16_t *>(q), w, row_seq,
+                                               row_pos, keys, fp8, key_scales, ids, n_valid,
+                                               scores, cand, stream),
+                      "index_scores launch");
+}
+
+int dsa_topk_pools(const dsa_config *cfg, int Q, int P, const float *scores, const uint8_t *cand,
+                   int32_t *sel, hipStream_t stream) {
+    clear_error();
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (Q < 0 || P < 0) return set_error(DSA_ERR_BAD_SIZE, "negative Q or P");
+    if (P > dsa::kTopkMaxPools)
+        return set_error(DSA_ERR_UNSUPPORTED, "topk_pools: rows of %d pools exceed the %d this kernel keeps",
+                    P, dsa::kTopkMaxPools);
+    const int Kw = (int)select_k(cfg, P);
+    if (Q == 0 || Kw == 0) return DSA_OK;
+    if (!scores || !cand || !sel) return set_error(DSA_ERR_NULL_ARG, "topk_pools: a buffer is NULL");
+    return hip_status(dsa::launch_topk_pools(Q, P, Kw, scores, cand, sel, stream),
+                      "topk_pools launch");
+}
+
+int dsa_expand_selection(const dsa_config *cfg, int Q, int Kw, int B, int S, int first_key,
+                         const int32_t *sel, const int32_t *row_seq, const int32_t *row_pos,
+                         const uint8_t *valid, int32_t *token_ids, hipStream_t stream) {
+    clear_error();
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (Q < 0 || Kw < 0 || B < 0 || S < 0 || first_key < 0) return set_error(DSA_ERR_BAD_SIZE, "negative size");
+    if ((int64_t)Kw * cfg->index_kpool > cfg->index_topk)
+        return set_error(DSA_ERR_BAD_SIZE, "expand_selection: %d pools of %d tokens exceed index_topk %d", Kw,
+                    cfg->index_kpool, cfg->index_topk);
+    const int64_t W = out_width(cfg);
+    if (Q == 0) return DSA_OK;
+    const bool tail = cfg->always_select_tail != 0;
+    if (!token_ids || (Kw > 0 && !sel) || (tail && (!row_seq || !row_pos || !valid)))
+        return set_error(DSA_ERR_NULL_ARG, "expand_selection: a buffer is NULL");
+    const int64_t P = num_pools(S, first_key, cfg->index_kpool);
+    return hip_status(dsa::launch_expand_selection(Q, Kw, cfg->index_kpool, cfg->index_topk, (int)W,
+                                                   tail, B, S, first_key, (int)P, sel, row_seq,
+                                                   row_pos, valid, token_ids, stream),
+                      "expand_selection launch");
+}
+
+size_t dsa_sparse_mla_decode_workspace(const dsa_config *cfg, int Q, int W) {
+    clear_error();
+    if (check_config(cfg) || Q < 0 || W < 0) return 0;
+    return dsa::plan_sparse_mla(Q, W, cfg->heads).ws_bytes;
+}
+
+int dsa_sparse_mla_decode(const dsa_config *cfg, int Q, int W, int B, float sm_scale,
+                          const void *q_abs, const int32_t *token_ids, const int32_t *row_seq,
+                          const void *kv, dsa_dtype kv_dtype, const float *kv_scales,
+                          int64_t kv_rows, int S, const int32_t *block_table, int max_blocks,
+                          int block_size, float *out, float *lse, void *ws, size_t ws_bytes,
+                          hipStream_t stream) {
+    clear_error();
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (Q < 0 || W < 0 || B < 0 || S < 0 || kv_rows < 0) return set_error(DSA_ERR_BAD_SIZE, "negative size");
+    if (kv_dtype != DSA_BF16 && kv_dtype != DSA_FP8_E4M3)
+        return set_error(DSA_ERR_BAD_DTYPE, "sparse_mla_decode: latent must be bf16 or fp8 e4m3");
+    if (Q == 0) return DSA_OK;
+    const bool fp8 = kv_dtype == DSA_FP8_E4M3;
+    if (!q_abs || !row_seq || !out || (W > 0 && !token_ids))
+        return set_error(DSA_ERR_NULL_ARG, "sparse_mla_decode: a buffer is NULL");
+    if (kv_rows > 0 && !kv) return set_error(DSA_ERR_NULL_ARG, "sparse_mla_decode: kv is NULL");
+    if (fp8 && kv_rows > 0 && !kv_scales)
+        return set_error(DSA_ERR_NULL_ARG, "sparse_mla_decode: fp8 latent needs kv_scales");
+    if (block_table) {
+        if (block_size <= 0 || max_blocks < 0)
+            return set_error(DSA_ERR_BAD_SIZE, "sparse_mla_decode: paged latent needs block_size > 0");
+    }
+    if (!aligned(q_abs, 16) || (kv && !aligned(kv, 16)) || !aligned(out, 16))
+        return set_error(DSA_ERR_BAD_SIZE, "sparse_mla_decode: q_abs, kv and out need 16-byte alignment");
+    const dsa::MlaPlan plan = dsa::plan_sparse_mla(Q, W, cfg->heads);
+    if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned(ws, 16)))
+        return set_error(DSA_ERR_WORKSPACE, "sparse_mla_decode: needs a 16-byte aligned workspace of %zu bytes",
+                    plan.ws_bytes);
+    return hip_status(dsa::launch_sparse_mla(plan, Q, W, cfg->heads, B, sm_scale,
+                                             static_cast<const uint16_t *>(q_abs), token_ids,
+                                             row_seq, kv, fp8, kv_scales, kv_rows, S, block_table,
+                                             max_blocks, block_size, out, lse, ws, stream),
+                      "sparse_mla_decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// dsa_launch.hpp -- internal launchers, one per kernel family. Arguments are already
+// checked by the C ABI layer (dsa_api.cpp); each launcher returns the HIP launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+hipError_t launch_kpool_compress(int B, int S, int D, int KP, int first_key, int P,
+                                 const uint16_t *k, const uint16_t *gate, const float *ape,
+                                 const uint8_t *valid, uint16_t *pool_keys, uint8_t *pool_valid,
+                                 hipStream_t stream);
+
+hipError_t launch_compact_pools(int B, int P, const uint8_t *pool_valid, int32_t *ids,
+                                int32_t *n_valid, hipStream_t stream);
+
+hipError_t launch_index_scores(int Q, int B, int P, int Hi, int D, int KP, int first_key,
+                               float scale, const uint16_t *q, const float *w,
+                               const int32_t *row_seq, const int32_t *row_pos, const void *keys,
+                               bool key_fp8, const float *key_scales, const int32_t *ids,
+                               const int32_t *n_valid, float *scores, uint8_t *cand,
+                               hipStream_t stream);
+
+// Largest row length the top-k kernel keeps in registers.
+constexpr int kTopkMaxPools = 65536;
+hipError_t launch_topk_pools(int Q, int P, int Kw, const float *scores, const uint8_t *cand,
+                             int32_t *sel, hipStream_t stream);
+
+hipError_t launch_expand_selection(int Q, int Kw, int KP, int topk, int W, bool tail, int B,
+                                   int S, int first_key, int P, const int32_t *sel,
+                                   const int32_t *row_seq, const int32_t *row_pos,
+                                   const uint8_t *valid, int32_t *token_ids, hipStream_t stream);
+
+struct MlaPlan {
+    int groups;      // 32-head groups
+    int splits;      // token splits per (row, group)
+    int split_len;   // token slots per split (multiple of 32)
+    size_t ws_bytes; // partial results for splits > 1
+};
+MlaPlan plan_sparse_mla(int Q, int W, int H);
+hipError_t launch_sparse_mla(const MlaPlan &plan, int Q, int W, int H, int B, float sm_scale,
+                             const uint16_t *q_abs, const int32_t *token_ids,
+                             const int32_t *row_seq, const void *kv, bool kv_fp8,
+                             const float *kv_scales, int64_t kv_rows, int S,
+                             const int32_t *block_table, int max_blocks, int block_size,
+                             float *out, float *lse, void *ws, hipStream_t stream);
+
+}  // namespace dsa

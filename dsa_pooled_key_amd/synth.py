@@ -29,21 +29,42 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Optional
 
 import numpy as np
 
 LATENT = 512
 BLOCK = 64
+_CHUNK = 1 << 22
+
+
+def _workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
 
 
 # ----------------------------------------------------------------------------- encodings
 
 def bf16_bits(x) -> np.ndarray:
-    """float32 -> bf16 bit pattern, round to nearest, ties to even (finite inputs)."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = u + 0x7FFF + ((u >> 16) & 1)
-    return ((rounded >> 16) & 0xFFFF).astype(np.uint16)
+    """float32 -> bf16 bit pattern, round to nearest, ties to even (finite inputs: the
+    largest finite pattern plus the rounding bias still fits in 32 bits)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    fi, fo = x.reshape(-1).view(np.uint32), out.reshape(-1)
+
+    def run(i):
+        u = fi[i:i + _CHUNK]
+        fo[i:i + _CHUNK] = ((u + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) >> 16).astype(np.uint16)
+
+    idx = range(0, fi.size, _CHUNK)
+    if len(idx) <= 1:
+        for i in idx:
+            run(i)
+    else:
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(run, idx))
+    return out
 
 
 def bf16_to_f32(bits) -> np.ndarray:
@@ -51,24 +72,31 @@ def bf16_to_f32(bits) -> np.ndarray:
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def _e4m3_chunk(x: np.ndarray) -> np.ndarray:
+    # Normal range: keep sign-less exponent + 3 mantissa bits of the binary32 pattern and
+    # round the 20 dropped bits to nearest even; rebias 127 -> 7 (subtract 120 << 3).
+    u = x.view(np.uint32)
+    sign = ((u >> 24) & 0x80).astype(np.uint8)
+    a = u & np.uint32(0x7FFFFFFF)
+    keep = (a >> 20).astype(np.int32)
+    rem = a & np.uint32(0xFFFFF)
+    up = (rem > 0x80000) | ((rem == 0x80000) & ((keep & 1) == 1))
+    code = np.clip(keep + up - 960, 0, 0x7E)
+    # Below 2^-6 (binary32 pattern 0x3C800000) the grid is multiples of 2^-9.
+    sub = a < np.uint32(0x3C800000)
+    code[sub] = np.rint(np.abs(x[sub]) * np.float32(512.0)).astype(np.int32)
+    return code.astype(np.uint8) | sign
+
+
 def e4m3_codes(x) -> np.ndarray:
     """float -> OCP e4m3 ("FN") code: round to nearest, ties to even, saturating at +-448.
     Subnormals are multiples of 2^-9 below 2^-6."""
-    x = np.asarray(x, np.float32)
-    sign = np.signbit(x).astype(np.uint8) << 7
-    a = np.minimum(np.abs(x).astype(np.float64), 448.0)
-    code = np.zeros(a.shape, np.uint8)
-    sub = a < 2.0 ** -6
-    code[sub] = np.rint(a[sub] * 512.0).astype(np.uint8)
-    nrm = ~sub
-    frac, ex = np.frexp(a[nrm])                 # a = frac * 2^ex, frac in [0.5, 1)
-    mant = np.rint(frac * 16.0).astype(np.int64)  # 8..16, i.e. 1.mmm in eighths
-    carry = mant == 16
-    mant[carry] = 8
-    ex = ex + carry
-    biased = ex + 6                              # value = mant/8 * 2^(ex-1), bias 7
-    code[nrm] = ((biased << 3) | (mant - 8)).astype(np.uint8)
-    return code | sign
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    fi, fo = x.reshape(-1), out.reshape(-1)
+    for i in range(0, fi.size, _CHUNK):
+        fo[i:i + _CHUNK] = _e4m3_chunk(fi[i:i + _CHUNK])
+    return out
 
 
 def e4m3_quantize_rows(x, exact_pow2: bool = False):
@@ -79,11 +107,17 @@ def e4m3_quantize_rows(x, exact_pow2: bool = False):
     amax = np.abs(x).max(axis=-1)
     s = (amax / np.float32(448.0)).astype(np.float32)
     if exact_pow2:
-        with np.errstate(divide="ignore"):
-            s = np.where(amax > 0, np.exp2(np.ceil(np.log2(np.maximum(s, 1e-30)))), 1.0)
-        s = s.astype(np.float32)
+        s = np.exp2(np.ceil(np.log2(np.maximum(s, np.float32(1e-30))))).astype(np.float32)
     s = np.where(amax > 0, s, np.float32(1.0)).astype(np.float32)
-    codes = e4m3_codes(x / s[..., None])
+    codes = np.empty(x.shape, np.uint8)
+    xr, cr, sr = x.reshape(-1, x.shape[-1]), codes.reshape(-1, x.shape[-1]), s.reshape(-1)
+    step = max(1, (1 << 22) // max(1, x.shape[-1]))
+
+    def run(i):
+        cr[i:i + step] = e4m3_codes(xr[i:i + step] / sr[i:i + step, None])
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(run, range(0, xr.shape[0], step)))
     return codes, s
 
 
@@ -113,7 +147,12 @@ class Workload:
     key_fp8: bool = False
     kv_fp8: bool = False
     paged: bool = False
-    prefill: bool = False
+    lengths: str = "full"  # full | minus3 | uniform_half | loguniform
+    invalid_rate: float = 0.0   # extra invalid slots below the length
+    rows: str = "decode"   # decode (one row per sequence at its last token) | prefill_tail
+                           # (the last Q positions of sequence 0) | mixed (random sequences
+                           # and positions, including positions before first_key)
+    plain: bool = False    # un-normalised keys and U(0.5, 1.5) head weights (the tiny recipe)
 
     @property
     def pools(self) -> int:
@@ -131,19 +170,35 @@ class Workload:
     def max_blocks(self) -> int:
         return (self.S + BLOCK - 1) // BLOCK
 
+    @property
+    def prefill(self) -> bool:
+        return self.rows != "decode"
+
 
 WORKLOADS = {
+    # The five measured workloads.
     "tiny": Workload("tiny", B=1, S=1024, Q=1, kpool=4, topk=64, index_heads=4, index_dim=32,
-                     heads=4),
+                     heads=4, lengths="minus3", plain=True),
     "decode_b8_32k": Workload("decode_b8_32k", B=8, S=32768, Q=8, kpool=4, topk=2048,
-                              index_heads=32, index_dim=128, heads=32),
+                              index_heads=32, index_dim=128, heads=32, lengths="uniform_half"),
     "decode_b4_256k": Workload("decode_b4_256k", B=4, S=262144, Q=4, kpool=4, topk=2048,
                                index_heads=32, index_dim=128, heads=32, paged=True),
     "prefill_2048_64k": Workload("prefill_2048_64k", B=1, S=65536, Q=2048, kpool=4, topk=2048,
-                                 index_heads=32, index_dim=128, heads=32, prefill=True),
+                                 index_heads=32, index_dim=128, heads=32, rows="prefill_tail"),
     "fp8_mixed_b32": Workload("fp8_mixed_b32", B=32, S=131072, Q=32, kpool=8, topk=4096,
                               index_heads=32, index_dim=128, heads=32, key_fp8=True,
-                              kv_fp8=True, paged=True),
+                              kv_fp8=True, paged=True, lengths="loguniform", invalid_rate=0.05),
+    # Small ragged workloads for parity at oracle-friendly sizes: sizes that are not multiples
+    # of any tile, first_key > 0, tail slots, head counts below and above 32.
+    "ragged_bf16": Workload("ragged_bf16", B=3, S=4999, Q=3, kpool=4, topk=200, index_heads=20,
+                            index_dim=64, heads=40, first_key=3, tail=True,
+                            lengths="uniform_half", invalid_rate=0.05),
+    "ragged_fp8": Workload("ragged_fp8", B=5, S=3001, Q=5, kpool=8, topk=160, index_heads=32,
+                           index_dim=128, heads=12, first_key=5, tail=True, key_fp8=True,
+                           kv_fp8=True, paged=True, lengths="loguniform", invalid_rate=0.05),
+    "ragged_prefill": Workload("ragged_prefill", B=2, S=2000, Q=70, kpool=2, topk=64,
+                               index_heads=32, index_dim=32, heads=32, first_key=1,
+                               lengths="uniform_half", rows="mixed"),
 }
 
 # Index score scale index_head_dim^-0.5 and MLA softmax scale qk_head_dim^-0.5 (qk_head_dim
@@ -156,58 +211,107 @@ def index_scale(wl: Workload, exact: bool) -> float:
 
 
 def _streams(seed: int, n: int):
-    return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(n)]
+    """n independent seed sequences, one per tensor, in a fixed order."""
+    return np.random.SeedSequence(seed).spawn(n)
 
 
-def _dyadic(rng, shape, denom: int, mmax: int) -> np.ndarray:
+def _rng(ss) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+def _chunked(ss, shape, fill) -> np.ndarray:
+    """A float32 array of `shape` filled in fixed 2^22-element chunks, chunk i from the i-th
+    child stream of `ss`; chunks run on a thread pool, so the values do not depend on the
+    number of threads."""
+    n = int(np.prod(shape))
+    out = np.empty(n, np.float32)
+    bounds = [(i, min(i + _CHUNK, n)) for i in range(0, n, _CHUNK)]
+    kids = ss.spawn(len(bounds))
+
+    def run(k):
+        i0, i1 = bounds[k]
+        fill(_rng(kids[k]), out[i0:i1])
+
+    if len(bounds) == 1:
+        run(0)
+    else:
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(run, range(len(bounds))))
+    return out.reshape(shape)
+
+
+def _normal(ss, shape, std: float = 1.0) -> np.ndarray:
+    """N(0, std^2) float32."""
+    def fill(g, o):
+        g.standard_normal(out=o, dtype=np.float32)
+        if std != 1.0:
+            o *= np.float32(std)
+    return _chunked(ss, shape, fill)
+
+
+def _dyadic(ss, shape, denom: int, mmax: int) -> np.ndarray:
     """Uniform integers in [-mmax, mmax] divided by denom, as float32."""
-    return (rng.integers(-mmax, mmax + 1, size=shape) / float(denom)).astype(np.float32)
+    def fill(g, o):
+        o[:] = g.integers(-mmax, mmax + 1, size=o.size).astype(np.float32) / np.float32(denom)
+    return _chunked(ss, shape, fill)
 
 
 def lengths(wl: Workload, rng) -> np.ndarray:
     """Valid length per sequence."""
-    if wl.name == "tiny":
-        return np.array([wl.S - 3], np.int64)
-    if wl.name == "decode_b8_32k":
+    if wl.lengths == "minus3":
+        return np.full(wl.B, wl.S - 3, np.int64)
+    if wl.lengths == "uniform_half":
         return rng.integers(wl.S // 2, wl.S + 1, size=wl.B).astype(np.int64)
-    if wl.name == "fp8_mixed_b32":
-        u = rng.uniform(math.log(4096), math.log(wl.S), size=wl.B)
-        return np.clip(np.rint(np.exp(u)), 4096, wl.S).astype(np.int64)
+    if wl.lengths == "loguniform":
+        lo = min(4096, max(1, wl.S // 32))
+        u = rng.uniform(math.log(lo), math.log(wl.S), size=wl.B)
+        return np.clip(np.rint(np.exp(u)), lo, wl.S).astype(np.int64)
     return np.full(wl.B, wl.S, np.int64)
 
 
 def validity(wl: Workload, L: np.ndarray, rng):
     """Token validity [B,S] and pool validity [B,P] drawn together.
 
-    For the mixed-length fp8 workload every slot below the length is invalid with
-    probability 0.05; this is sampled pool by pool: a pool wholly below the length is drawn
-    all-valid with probability 0.95^kpool, otherwise its slots are drawn from the
-    distribution conditioned on at least one invalid slot. Elsewhere slots are valid exactly
-    below the length. Pool validity is the drawn all-valid event, so it is not computed from
-    the token mask here."""
+    With an invalid rate e, every slot below the length is invalid with probability e;
+    this is sampled pool by pool: a pool wholly below the length is drawn all-valid with
+    probability (1-e)^kpool, otherwise its slots are drawn from the distribution conditioned
+    on at least one invalid slot. Without it, slots are valid exactly below the length.
+    Pool validity is the drawn all-valid event, so it is not computed from the token mask."""
     B, S, KP, f, P = wl.B, wl.S, wl.kpool, wl.first_key, wl.pools
+    e = wl.invalid_rate
     valid = np.zeros((B, S), np.uint8)
     pool_valid = np.zeros((B, P), np.uint8)
     for b in range(B):
         Lb = int(L[b])
         valid[b, :Lb] = 1
         whole = max(0, (Lb - f) // KP)
-        if wl.name == "fp8_mixed_b32":
-            p_ok = 0.95 ** KP
-            ok = rng.random(whole) < p_ok
+        if e > 0:
+            ok = rng.random(whole) < (1.0 - e) ** KP
             pool_valid[b, :whole] = ok
-            bad = np.nonzero(~ok)[0]
-            for p in bad:
+            for p in np.nonzero(~ok)[0]:
                 while True:
-                    slot_ok = rng.random(KP) >= 0.05
+                    slot_ok = rng.random(KP) >= e
                     if not slot_ok.all():
                         break
                 valid[b, f + p * KP: f + (p + 1) * KP] = slot_ok
-            rest = np.arange(f + whole * KP, Lb)
-            valid[b, rest] = rng.random(rest.size) >= 0.05
+            rest = np.r_[np.arange(0, min(f, Lb)), np.arange(f + whole * KP, Lb)]
+            valid[b, rest] = rng.random(rest.size) >= e
         else:
             pool_valid[b, :whole] = 1
     return valid, pool_valid
+
+
+def query_rows(wl: Workload, L: np.ndarray, rng):
+    """(row_seq, row_pos) of the query rows."""
+    Q = wl.Q
+    if wl.rows == "prefill_tail":
+        return np.zeros(Q, np.int32), (wl.S - Q + np.arange(Q)).astype(np.int32)
+    if wl.rows == "mixed":
+        seq = rng.integers(0, wl.B, Q).astype(np.int32)
+        pos = np.array([rng.integers(0, L[b]) for b in seq], np.int32)
+        pos[:2] = [0, max(0, wl.first_key - 1)]          # rows with no whole pool yet
+        return seq, pos
+    return np.arange(Q, dtype=np.int32), (L[:Q] - 1).astype(np.int32)
 
 
 @dataclasses.dataclass
@@ -238,13 +342,10 @@ class DecodeInputs:
 
 
 def _layout_kv(wl: Workload, L: np.ndarray, rng_perm):
-    """Rows of the latent cache and, for paged workloads, the block table."""
+    """Rows of the latent cache and, for paged workloads, the block table: each sequence
+    owns ceil(L_b / 64) blocks, all blocks shuffled across sequences; unmapped entries -1."""
     if not wl.paged:
         return wl.B * wl.S, None
-    if wl.name == "decode_b4_256k":
-        nblk = wl.B * wl.max_blocks
-        perm = rng_perm.permutation(nblk).astype(np.int32)
-        return nblk * BLOCK, perm.reshape(wl.B, wl.max_blocks)
     need = [int((int(l) + BLOCK - 1) // BLOCK) for l in L]
     total = int(sum(need))
     perm = rng_perm.permutation(total).astype(np.int32)
@@ -258,67 +359,60 @@ def _layout_kv(wl: Workload, L: np.ndarray, rng_perm):
 
 def make_decode_inputs(name: str, seed: int = 0, exact: bool = False) -> DecodeInputs:
     wl = WORKLOADS[name]
-    (r_len, r_valid, r_keys, r_q, r_w, r_qabs, r_kv, r_perm) = _streams(seed, 8)
-    L = lengths(wl, r_len)
-    valid, pool_valid = validity(wl, L, r_valid)
+    (s_len, s_valid, s_keys, s_kscale, s_q, s_w, s_qabs, s_kv, s_kvscale,
+     s_perm, s_rows) = _streams(seed, 11)
+    L = lengths(wl, _rng(s_len))
+    valid, pool_valid = validity(wl, L, _rng(s_valid))
     B, P, D, Q, Hi, H = wl.B, wl.pools, wl.index_dim, wl.Q, wl.index_heads, wl.heads
 
     # pooled keys
     key_scales = None
     if exact:
         if wl.key_fp8:
-            kf = _dyadic(r_keys, (B, P, D), 8, 8)
-            keys = e4m3_codes(kf)
-            key_scales = np.exp2(r_keys.integers(-2, 2, size=(B, P))).astype(np.float32)
+            keys = e4m3_codes(_dyadic(s_keys, (B, P, D), 8, 8))
+            key_scales = np.exp2(_rng(s_kscale).integers(-2, 2, size=(B, P))).astype(np.float32)
         else:
-            keys = bf16_bits(_dyadic(r_keys, (B, P, D), 16, 16))
+            keys = bf16_bits(_dyadic(s_keys, (B, P, D), 16, 16))
     else:
-        kf = layer_norm_f32(r_keys.standard_normal((B, P, D), dtype=np.float32))
+        kf = _normal(s_keys, (B, P, D))
+        if not wl.plain:
+            kf = layer_norm_f32(kf)
         if wl.key_fp8:
             keys, key_scales = e4m3_quantize_rows(kf)
-        elif wl.name == "tiny":
-            keys = bf16_bits(r_keys.standard_normal((B, P, D), dtype=np.float32))
         else:
             keys = bf16_bits(kf)
 
     # queries and head weights
     if exact:
-        q = bf16_bits(_dyadic(r_q, (Q, Hi, D), 4, 4))
-        w = _dyadic(r_w, (Q, Hi), 8, 12)
+        q = bf16_bits(_dyadic(s_q, (Q, Hi, D), 4, 4))
+        w = _dyadic(s_w, (Q, Hi), 8, 12)
     else:
-        q = bf16_bits(r_q.standard_normal((Q, Hi, D), dtype=np.float32))
-        if wl.name == "tiny":
-            w = r_w.uniform(0.5, 1.5, size=(Q, Hi)).astype(np.float32)
+        q = bf16_bits(_normal(s_q, (Q, Hi, D)))
+        if wl.plain:
+            w = _rng(s_w).uniform(0.5, 1.5, size=(Q, Hi)).astype(np.float32)
         else:
-            w = (r_w.standard_normal((Q, Hi), dtype=np.float32) *
-                 np.float32(Hi ** -0.5)).astype(np.float32)
+            w = (_normal(s_w, (Q, Hi)) * np.float32(Hi ** -0.5)).astype(np.float32)
 
-    if wl.prefill:
-        row_seq = np.zeros(Q, np.int32)
-        row_pos = (wl.S - Q + np.arange(Q)).astype(np.int32)
-    else:
-        row_seq = np.arange(Q, dtype=np.int32)
-        row_pos = (L - 1).astype(np.int32)
+    row_seq, row_pos = query_rows(wl, L, _rng(s_rows))
 
     # latent side
     if exact:
-        q_abs = bf16_bits(_dyadic(r_qabs, (Q, H, LATENT), 4, 4))
+        q_abs = bf16_bits(_dyadic(s_qabs, (Q, H, LATENT), 4, 4))
     else:
-        q_abs = bf16_bits(r_qabs.standard_normal((Q, H, LATENT), dtype=np.float32) * 0.5)
-    rows, table = _layout_kv(wl, L, r_perm)
+        q_abs = bf16_bits(_normal(s_qabs, (Q, H, LATENT), 0.5))
+    rows, table = _layout_kv(wl, L, _rng(s_perm))
     kv_scales = None
     if wl.kv_fp8:
         if exact:
-            kv = e4m3_codes(_dyadic(r_kv, (rows, LATENT), 8, 8))
-            kv_scales = np.exp2(r_kv.integers(-2, 2, size=rows)).astype(np.float32)
+            kv = e4m3_codes(_dyadic(s_kv, (rows, LATENT), 8, 8))
+            kv_scales = np.exp2(_rng(s_kvscale).integers(-2, 2, size=rows)).astype(np.float32)
         else:
-            kv, kv_scales = e4m3_quantize_rows(
-                r_kv.standard_normal((rows, LATENT), dtype=np.float32) * np.float32(0.5))
+            kv, kv_scales = e4m3_quantize_rows(_normal(s_kv, (rows, LATENT), 0.5))
     else:
         if exact:
-            kv = bf16_bits(_dyadic(r_kv, (rows, LATENT), 4, 4))
+            kv = bf16_bits(_dyadic(s_kv, (rows, LATENT), 4, 4))
         else:
-            kv = bf16_bits(r_kv.standard_normal((rows, LATENT), dtype=np.float32) * 0.5)
+            kv = bf16_bits(_normal(s_kv, (rows, LATENT), 0.5))
     return DecodeInputs(wl=wl, exact=exact, lengths=L, valid=valid, pool_valid=pool_valid,
                         keys=keys, key_scales=key_scales, q=q, w=w, row_seq=row_seq,
                         row_pos=row_pos, q_abs=q_abs, kv=kv, kv_scales=kv_scales,
@@ -339,29 +433,52 @@ class KpoolInputs:
 def make_kpool_inputs(name: str, seed: int = 0, exact: bool = False,
                       batch: Optional[int] = None) -> KpoolInputs:
     """Token keys (LayerNorm'd N(0,1) rows; plain N(0,1) for ``tiny``), gate N(0,1), ape
-    N(0,1) and the workload's validity. ``batch`` keeps only the first sequences.
+    N(0,1) and the workload's validity (the same lengths and token mask as
+    make_decode_inputs with the same seed). ``batch`` keeps only the first sequences.
     The exact twin has keys in multiples of 1/4, gate 0, and ape either 0 (uniform pool
     weights, kpool 4) or +-64 on one slot per channel (one-hot weights, kpool 8), so pooled
     keys are exact in bf16 and in e4m3."""
     wl = WORKLOADS[name]
-    (r_len, r_valid, r_k, r_gate, r_ape, r_hot) = _streams(seed + 1000, 6)
-    L = lengths(wl, r_len)
-    valid, _ = validity(wl, L, r_valid)
+    s_len, s_valid = _streams(seed, 11)[:2]          # the decode inputs' lengths and masks
+    (s_k, s_gate, s_ape, s_hot) = _streams(seed + 1000, 4)
+    L = lengths(wl, _rng(s_len))
+    valid, _ = validity(wl, L, _rng(s_valid))
     B = wl.B if batch is None else min(batch, wl.B)
-    valid = valid[:B]
+    valid = np.ascontiguousarray(valid[:B])
     shape = (B, wl.S, wl.index_dim)
     if exact:
-        k = bf16_bits(_dyadic(r_k, shape, 4, 4))
+        k = bf16_bits(_dyadic(s_k, shape, 4, 4))
         gate = np.zeros(shape, np.uint16)
         if wl.kpool == 8:
-            hot = r_hot.integers(0, wl.kpool, size=wl.index_dim)
+            hot = _rng(s_hot).integers(0, wl.kpool, size=wl.index_dim)
             ape = np.full((wl.kpool, wl.index_dim), -64.0, np.float32)
             ape[hot, np.arange(wl.index_dim)] = 64.0
         else:
             ape = np.zeros((wl.kpool, wl.index_dim), np.float32)
     else:
-        kf = r_k.standard_normal(shape, dtype=np.float32)
-        k = bf16_bits(kf if wl.name == "tiny" else layer_norm_f32(kf))
-        gate = bf16_bits(r_gate.standard_normal(shape, dtype=np.float32))
-        ape = r_ape.standard_normal((wl.kpool, wl.index_dim), dtype=np.float32)
+        kf = _normal(s_k, shape)
+        k = bf16_bits(kf if wl.plain else layer_norm_f32(kf))
+        gate = bf16_bits(_normal(s_gate, shape))
+        ape = _normal(s_ape, (wl.kpool, wl.index_dim))
     return KpoolInputs(wl=wl, exact=exact, k=k, gate=gate, ape=ape, valid=valid)
+
+
+def draw_token_ids(di: DecodeInputs, seed: int = 7, holes: float = 0.02) -> np.ndarray:
+    """Synthetic attention sets for the sparse-MLA stage alone: per row, up to out_width
+    distinct valid tokens at or before the row's position, ascending, a few slots replaced by
+    -1, and -1 padding at the end (a row at a position with no valid token gets none).
+    [Q, out_width] int32."""
+    wl = di.wl
+    rng = _rng(np.random.SeedSequence(seed))
+    W = wl.width
+    out = np.full((wl.Q, W), -1, np.int32)
+    for r in range(wl.Q):
+        b, pos = int(di.row_seq[r]), int(di.row_pos[r])
+        pool = np.nonzero(di.valid[b, :pos + 1])[0]
+        if pool.size == 0:
+            continue
+        n = int(min(W, pool.size) * rng.uniform(0.8, 1.0)) if r % 3 == 2 else min(W, pool.size)
+        pick = np.sort(rng.choice(pool, size=n, replace=False)).astype(np.int32)
+        pick[rng.random(n) < holes] = -1
+        out[r, :n] = pick
+    return out

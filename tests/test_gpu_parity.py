@@ -1,0 +1,365 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, stage by stage.
+
+Each GPU stage gets the same input bytes as the oracle stage it is compared with. Inputs
+come from the seeded generators or from the oracle's own previous stage, never from the GPU.
+
+* integer / index work (compact, top-k, expand, selections on exact twins): bit-exact;
+* index scores: |gpu - ref| <= 1e-3 |ref| + 1e-3 max_row |ref| (exact twins: bit-exact);
+* pooled keys: within one bf16 ulp (+1e-6), exact twins bit-exact;
+* sparse MLA: |gpu - ref| <= 2e-2 + 1e-2 |ref| with a bf16 latent, 5e-2 + 1e-2 |ref| fp8.
+
+Full-size workloads run on the GPU exactly as the benchmark launches them; the oracle checks
+sampled rows where all rows would take too long.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dsa_pooled_key_amd import binding as dsa
+from dsa_pooled_key_amd import synth
+from dsa_pooled_key_amd.pipeline import DecodeStep, DeviceDecodeInputs, config_for
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["tiny", "ragged_bf16", "ragged_fp8", "ragged_prefill"]
+FULL = ["decode_b8_32k", "decode_b4_256k", "prefill_2048_64k", "fp8_mixed_b32"]
+ALL = SMALL + FULL
+
+_CACHE = {}
+
+
+def setup_module():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU parity tests need a GPU")
+    print(f"\n[gpu] {torch.cuda.get_device_name(0)} libdsa: {dsa.version()}", flush=True)
+
+
+def case(name, exact=False):
+    key = (name, exact)
+    if key not in _CACHE:
+        print(f"\n[gpu] generating {name} exact={exact}", flush=True)
+        di = synth.make_decode_inputs(name, exact=exact)
+        x = DeviceDecodeInputs.upload(di)
+        ids, nv = oracle.compact_pools(di.pool_valid)
+        _CACHE[key] = (di, x, ids, nv)
+    return _CACHE[key]
+
+
+def _rows(di, n_small, seed=0):
+    Q = di.wl.Q
+    if Q <= n_small + 2:
+        return np.arange(Q)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, Q - 1), size=n_small, replace=False)
+    return np.unique(np.r_[0, mid, Q - 1])
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _oracle_scores(di, ids, nv, rows):
+    wl = di.wl
+    return oracle.index_scores(di.q[rows], di.w[rows], di.row_seq[rows], di.row_pos[rows],
+                               di.keys, ids, nv, kpool=wl.kpool, first_key=wl.first_key,
+                               scale=di.scale, key_scales=di.key_scales)
+
+
+def _check_scores(gs, rs, rc):
+    for r in range(rs.shape[0]):
+        on = rc[r] == 1
+        if not on.any():
+            continue
+        ref = rs[r, on].astype(np.float64)
+        got = gs[r, on].astype(np.float64)
+        tol = 1e-3 * np.abs(ref) + 1e-3 * np.abs(ref).max()
+        bad = np.abs(got - ref) > tol
+        assert not bad.any(), (r, np.nonzero(on)[0][bad][:5], got[bad][:5], ref[bad][:5])
+
+
+def _check_mla(go, gl, ro, rl, fp8):
+    atol = 5e-2 if fp8 else 2e-2
+    err = np.abs(go.astype(np.float64) - ro) - (atol + 1e-2 * np.abs(ro))
+    assert err.max() <= 0, (np.unravel_index(err.argmax(), err.shape), err.max())
+    both_inf = np.isneginf(gl) & np.isneginf(rl)
+    assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
+    assert np.allclose(gl[~both_inf], rl[~both_inf], rtol=1e-4, atol=1e-4)
+
+
+# ------------------------------------------------------------------ step 2: compact_pools
+
+@pytest.mark.parametrize("name", ALL)
+def test_compact_pools_bit_exact(name):
+    di, x, ids, nv = case(name)
+    g_ids, g_nv = dsa.compact_pools(x.pool_valid)
+    assert np.array_equal(g_nv.cpu().numpy(), nv)
+    assert np.array_equal(g_ids.cpu().numpy(), ids)
+
+
+# ------------------------------------------------------------------ step 3: index_scores
+
+@pytest.mark.parametrize("name", ALL)
+def test_index_scores(name):
+    di, x, ids, nv = case(name)
+    wl = di.wl
+    cfg = config_for(wl)
+    scores, cand = dsa.index_scores(cfg, x.q, x.w, x.row_seq, x.row_pos, x.keys, _dev(ids),
+                                    _dev(nv), first_key=wl.first_key, scale=di.scale,
+                                    key_scales=x.key_scales)
+    rows = _rows(di, 14)
+    rs, rc = _oracle_scores(di, ids, nv, rows)
+    gs, gc = scores.cpu().numpy()[rows], cand.cpu().numpy()[rows]
+    assert np.array_equal(gc, rc)
+    assert np.all(np.isneginf(gs[rc == 0]))
+    assert not np.any(np.signbit(gs[rc == 1]) & (gs[rc == 1] == 0))
+    _check_scores(gs, rs, rc)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_index_scores_exact_twin_bit_exact(name):
+    di, x, ids, nv = case(name, exact=True)
+    wl = di.wl
+    cfg = config_for(wl)
+    scores, cand = dsa.index_scores(cfg, x.q, x.w, x.row_seq, x.row_pos, x.keys, _dev(ids),
+                                    _dev(nv), first_key=wl.first_key, scale=di.scale,
+                                    key_scales=x.key_scales)
+    rows = _rows(di, 6)
+    rs, rc = _oracle_scores(di, ids, nv, rows)
+    gs, gc = scores.cpu().numpy()[rows], cand.cpu().numpy()[rows]
+    assert np.array_equal(gc, rc)
+    assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32))
+
+
+# ------------------------------------------------------------------ steps 4 and 5
+
+@pytest.mark.parametrize("name", ALL)
+def test_topk_and_expand_bit_exact_on_oracle_scores(name):
+    di, x, ids, nv = case(name)
+    wl = di.wl
+    cfg = config_for(wl)
+    rows = _rows(di, 14)
+    rs, rc = _oracle_scores(di, ids, nv, rows)
+    sel_ref = oracle.topk_pools(rs, rc, wl.kw)
+    sel = dsa.topk_pools(cfg, _dev(rs), _dev(rc))
+    assert np.array_equal(sel.cpu().numpy(), sel_ref)
+    tok_ref = oracle.expand_selection(sel_ref, di.row_seq[rows], di.row_pos[rows], di.valid,
+                                      kpool=wl.kpool, index_topk=wl.topk,
+                                      always_select_tail=wl.tail, first_key=wl.first_key)
+    tok = dsa.expand_selection(cfg, _dev(sel_ref), _dev(di.row_seq[rows]),
+                               _dev(di.row_pos[rows]), x.valid, S=wl.S, first_key=wl.first_key)
+    assert np.array_equal(tok.cpu().numpy(), tok_ref)
+
+
+@pytest.mark.parametrize("P,kw,seed", [(1, 1, 0), (100, 7, 1), (1024, 512, 2), (1025, 512, 3),
+                                       (5000, 300, 4), (16384, 512, 5), (32769, 512, 6),
+                                       (65536, 512, 7), (65536, 1, 8), (3000, 3000, 9)])
+def test_topk_ties_signs_and_row_lengths(P, kw, seed):
+    rng = np.random.default_rng(seed)
+    Q = 6
+    scores = (rng.integers(-40, 41, (Q, P)) / 8.0).astype(np.float32)   # heavy ties
+    scores[1] = 0.0
+    scores[1, ::3] = -0.0                                                # signed zeros tie
+    scores[2] = rng.standard_normal(P).astype(np.float32) * 1e-30        # tiny magnitudes
+    scores[3] = -np.abs(rng.standard_normal(P)).astype(np.float32)       # all negative
+    cand = (rng.random((Q, P)) < 0.7).astype(np.uint8)
+    cand[4] = 0
+    cand[4, : max(1, kw // 2)] = 1                                       # fewer than kw
+    cand[5] = 0                                                          # none
+    scores[cand == 0] = -np.inf
+    cfg = dsa.Config.make(index_heads=32, index_head_dim=128, index_kpool=1, index_topk=kw,
+                          heads=32)
+    got = dsa.topk_pools(cfg, _dev(scores), _dev(cand)).cpu().numpy()
+    assert np.array_equal(got, oracle.topk_pools(scores, cand, min(kw, P)))
+
+
+# ------------------------------------------------------------------ step 6: sparse MLA
+
+@pytest.mark.parametrize("name", ALL)
+def test_sparse_mla_decode(name):
+    di, x, _, _ = case(name)
+    wl = di.wl
+    cfg = config_for(wl)
+    tok = synth.draw_token_ids(di)
+    out, lse = dsa.sparse_mla_decode(cfg, x.q_abs, _dev(tok), x.row_seq, x.kv, B=wl.B,
+                                     sm_scale=di.sm_scale, S=wl.S, kv_scales=x.kv_scales,
+                                     block_table=x.block_table)
+    rows = _rows(di, 64)
+    ro, rl = oracle.sparse_mla(di.q_abs[rows], tok[rows], di.row_seq[rows], di.kv,
+                               sm_scale=di.sm_scale, S=wl.S, kv_scales=di.kv_scales,
+                               block_table=di.block_table)
+    _check_mla(out.cpu().numpy()[rows], lse.cpu().numpy()[rows], ro, rl, wl.kv_fp8)
+
+
+def test_sparse_mla_repeatable_paging_invariant_and_masks_bad_ids():
+    di, x, _, _ = case("ragged_bf16")
+    wl = di.wl
+    cfg = config_for(wl)
+    tok = synth.draw_token_ids(di)
+    kw = dict(B=wl.B, sm_scale=di.sm_scale, S=wl.S)
+    o1, l1 = dsa.sparse_mla_decode(cfg, x.q_abs, _dev(tok), x.row_seq, x.kv, **kw)
+    o2, l2 = dsa.sparse_mla_decode(cfg, x.q_abs, _dev(tok), x.row_seq, x.kv, **kw)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # the same rows behind a shuffled 64-token block table: identical bits
+    bs = 64
+    nb = (wl.S + bs - 1) // bs
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(wl.B * nb).astype(np.int32)
+    table = perm.reshape(wl.B, nb)
+    paged = np.zeros((wl.B * nb * bs, 512), np.uint16)
+    for b in range(wl.B):
+        for j in range(nb):
+            n = min(bs, wl.S - j * bs)
+            paged[table[b, j] * bs: table[b, j] * bs + n] = di.kv[b * wl.S + j * bs: b * wl.S + j * bs + n]
+    kvp = torch.from_numpy(paged.view(np.int16)).cuda().view(torch.bfloat16)
+    o3, l3 = dsa.sparse_mla_decode(cfg, x.q_abs, _dev(tok), x.row_seq, kvp, B=wl.B,
+                                   sm_scale=di.sm_scale, S=wl.S, block_table=_dev(table))
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    # ids past the sequence, negative ids and unmapped blocks are skipped like -1
+    bad = tok.copy()
+    bad[0, 5] = wl.S + 10
+    bad[1, 7] = -5
+    table2 = table.copy()
+    blk = int(tok[2, 3]) // bs
+    table2[int(di.row_seq[2]), blk] = -1
+    clean = bad.copy()
+    clean[clean >= wl.S] = -1
+    clean[clean < 0] = -1
+    clean[2][(tok[2] >= 0) & (tok[2] // bs == blk)] = -1
+    o4, l4 = dsa.sparse_mla_decode(cfg, x.q_abs, _dev(bad), x.row_seq, kvp, B=wl.B,
+                                   sm_scale=di.sm_scale, S=wl.S, block_table=_dev(table2))
+    ro, rl = oracle.sparse_mla(di.q_abs, clean, di.row_seq, di.kv, sm_scale=di.sm_scale, S=wl.S)
+    _check_mla(o4.cpu().numpy(), l4.cpu().numpy(), ro, rl, False)
+    # empty rows
+    empty = np.full_like(tok, -1)
+    o5, l5 = dsa.sparse_mla_decode(cfg, x.q_abs, _dev(empty), x.row_seq, x.kv, **kw)
+    assert torch.all(o5 == 0) and torch.all(torch.isneginf(l5))
+
+
+# ------------------------------------------------------------------ step 1: kpool_compress
+
+KPOOL_BATCH = {"fp8_mixed_b32": 6, "decode_b4_256k": 2}
+
+
+@pytest.mark.parametrize("exact", [False, True])
+@pytest.mark.parametrize("name", ALL)
+def test_kpool_compress(name, exact):
+    ki = synth.make_kpool_inputs(name, exact=exact, batch=KPOOL_BATCH.get(name))
+    wl = ki.wl
+    cfg = config_for(wl)
+    k = _dev(ki.k.view(np.int16)).view(torch.bfloat16)
+    g = _dev(ki.gate.view(np.int16)).view(torch.bfloat16)
+    pk, pv = dsa.kpool_compress(cfg, k, g, _dev(ki.ape), _dev(ki.valid), wl.first_key)
+    rk, rv = oracle.kpool_compress(ki.k, ki.gate, ki.ape, ki.valid, wl.kpool, wl.first_key)
+    assert np.array_equal(pv.cpu().numpy(), rv)
+    got = pk.view(torch.int16).cpu().numpy().view(np.uint16)
+    a = synth.bf16_to_f32(got).astype(np.float64)
+    b = synth.bf16_to_f32(rk).astype(np.float64)
+    if exact:
+        # Compared by value: with one-hot weights the exact pooled key is the hot slot's key
+        # plus about 1e-56 times the others, which the f64 oracle rounds to -0 when the hot key
+        # is 0 and the GPU, whose exp(-128) underflows to 0 in f32, writes as +0.
+        assert np.array_equal(a, b)
+        return
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(b), 2.0 ** -126))) - 7)
+    bad = np.abs(a - b) > ulp + 1e-6
+    assert not bad.any(), (np.argwhere(bad)[:4], a[bad][:4], b[bad][:4])
+
+
+# ------------------------------------------------------------------ chains
+
+def _oracle_select(di, ids, nv, rows):
+    wl = di.wl
+    rs, rc = _oracle_scores(di, ids, nv, rows)
+    sel = oracle.topk_pools(rs, rc, wl.kw)
+    tok = oracle.expand_selection(sel, di.row_seq[rows], di.row_pos[rows], di.valid,
+                                  kpool=wl.kpool, index_topk=wl.topk,
+                                  always_select_tail=wl.tail, first_key=wl.first_key)
+    return rs, rc, sel, tok
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_selection_chain_exact_twin_bit_exact(name):
+    di, x, ids, nv = case(name, exact=True)
+    step = DecodeStep(di.wl, x, di.scale, di.sm_scale)
+    step.select()
+    rows = _rows(di, 6)
+    _, _, sel, tok = _oracle_select(di, ids, nv, rows)
+    assert np.array_equal(step.sel.cpu().numpy()[rows], sel)
+    assert np.array_equal(step.token_ids.cpu().numpy()[rows], tok)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_selection_chain_general_differs_only_at_the_cutoff(name):
+    di, x, ids, nv = case(name)
+    step = DecodeStep(di.wl, x, di.scale, di.sm_scale)
+    step.select()
+    rows = _rows(di, 6)
+    rs, rc, sel, _ = _oracle_select(di, ids, nv, rows)
+    gsel = step.sel.cpu().numpy()[rows]
+    for i in range(len(rows)):
+        a = set(int(p) for p in sel[i] if p >= 0)
+        b = set(int(p) for p in gsel[i] if p >= 0)
+        assert len(a) == len(b)
+        assert all(rc[i, p] for p in b)
+        assert list(gsel[i][: len(b)]) == sorted(b)
+        diff = a ^ b
+        if diff:
+            cutoff = min(rs[i, p] for p in a)
+            span = max(abs(cutoff), np.abs(rs[i][rc[i] == 1]).max())
+            assert all(abs(rs[i, p] - cutoff) <= 1e-3 * span for p in diff), (i, diff)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_bf16", "ragged_prefill"])
+def test_full_path_from_token_cache_exact_twin(name):
+    """kpool_compress -> compact -> scores -> top-k -> expand -> MLA, each side on its own
+    outputs, starting from the same token-level cache: ids bit-exact, output in tolerance."""
+    di = synth.make_decode_inputs(name, exact=True)
+    ki = synth.make_kpool_inputs(name, exact=True)
+    wl = di.wl
+    cfg = config_for(wl)
+    x = DeviceDecodeInputs.upload(di)
+    k = _dev(ki.k.view(np.int16)).view(torch.bfloat16)
+    g = _dev(ki.gate.view(np.int16)).view(torch.bfloat16)
+    pk, pv = dsa.kpool_compress(cfg, k, g, _dev(ki.ape), _dev(ki.valid), wl.first_key)
+    x.keys, x.pool_valid, x.key_scales, x.valid = pk, pv, None, _dev(ki.valid)
+    step = DecodeStep(wl, x, di.scale, di.sm_scale)
+    step.run()
+    rk, rv = oracle.kpool_compress(ki.k, ki.gate, ki.ape, ki.valid, wl.kpool, wl.first_key)
+    ids, nv = oracle.compact_pools(rv)
+    rs, rc = oracle.index_scores(di.q, di.w, di.row_seq, di.row_pos, rk, ids, nv,
+                                 kpool=wl.kpool, first_key=wl.first_key, scale=di.scale)
+    sel = oracle.topk_pools(rs, rc, wl.kw)
+    tok = oracle.expand_selection(sel, di.row_seq, di.row_pos, ki.valid, kpool=wl.kpool,
+                                  index_topk=wl.topk, always_select_tail=wl.tail,
+                                  first_key=wl.first_key)
+    assert np.array_equal(step.sel.cpu().numpy(), sel)
+    assert np.array_equal(step.token_ids.cpu().numpy(), tok)
+    ro, rl = oracle.sparse_mla(di.q_abs, tok, di.row_seq, di.kv, sm_scale=di.sm_scale, S=wl.S,
+                               kv_scales=di.kv_scales, block_table=di.block_table)
+    _check_mla(step.out.cpu().numpy(), step.lse.cpu().numpy(), ro, rl, wl.kv_fp8)
+
+
+@pytest.mark.parametrize("name", ["ragged_fp8", "fp8_mixed_b32"])
+def test_decode_step_graph_replay_matches_eager(name):
+    di, x, _, _ = case(name)
+    step = DecodeStep(di.wl, x, di.scale, di.sm_scale)
+    step.run()
+    torch.cuda.synchronize()
+    ref = (step.sel.clone(), step.token_ids.clone(), step.out.clone(), step.lse.clone())
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step.run()
+    torch.cuda.current_stream().wait_stream(s)
+    with torch.cuda.graph(graph):
+        step.run()
+    for _ in range(3):
+        step.out.zero_()
+        step.sel.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(step.sel, ref[0]) and torch.equal(step.token_ids, ref[1])
+        assert torch.equal(step.out, ref[2]) and torch.equal(step.lse, ref[3])

@@ -1,0 +1,192 @@
+"""Host-side checks of libdsa that need no GPU: the shared library loads and exports every
+function include/dsa.h declares; the config rules, geometry helpers, host weight transforms
+and bf16 rounding agree with the oracle; and every argument refusal returns its code
+without launching anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from dsa_pooled_key_amd import binding as dsa
+from dsa_pooled_key_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return [l.split() for l in fh if l.strip() and not l.startswith("#")]
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = dsa.lib()
+    names = _declared()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(dsa.EXPORTED)
+    assert dsa.version().startswith("dsa ")
+
+
+def _cfg(**kw):
+    base = dict(index_heads=32, index_head_dim=128, index_kpool=4, index_topk=2048, heads=32)
+    base.update(kw)
+    return dsa.Config.make(**base)
+
+
+RULE_TO_CODE = {0: 0, 1: -4, 2: -5, 3: -6, 4: -7, 5: -8, 6: -9}
+
+
+def test_validate_matches_oracle_and_page_order():
+    for kp, tk, kvl, heads, rule in _rows("validate_cases.txt"):
+        cfg = _cfg(index_kpool=int(kp), index_topk=int(tk), kv_lora_rank=int(kvl),
+                   heads=int(heads))
+        assert dsa.config_validate(cfg) == RULE_TO_CODE[int(rule)], (kp, tk, kvl, heads)
+        assert oracle.validate(int(kp), int(tk), int(kvl), int(heads)) == int(rule)
+
+
+def test_geometry_matches_oracle():
+    for tk, kp, n, tail, sk, ow in _rows("geometry_cases.txt"):
+        cfg = _cfg(index_kpool=int(kp), index_topk=int(tk), always_select_tail=bool(int(tail)))
+        assert dsa.select_k(cfg, int(n)) == int(sk) == oracle.select_k(int(tk), int(kp), int(n))
+        assert dsa.out_width(cfg) == int(ow)
+    for S, f, kp in [(1024, 0, 4), (1023, 0, 4), (1024, 3, 4), (3, 0, 4), (262144, 0, 4),
+                     (131072, 0, 8), (5, 5, 1)]:
+        assert dsa.num_pools(S, f, kp) == oracle.num_pools(S, f, kp)
+    with pytest.raises(dsa.DsaError):
+        dsa.num_pools(10, 0, 0)
+
+
+def _absorb_case(seed, heads=3, nope=8, vd=6, kvl=512, ql=24, hidden=10):
+    rng = np.random.default_rng(seed)
+    q_b = rng.standard_normal((heads * nope, ql)).astype(np.float32)
+    kv_b = rng.standard_normal((heads * (nope + vd), kvl)).astype(np.float32)
+    o = rng.standard_normal((hidden, heads * vd)).astype(np.float32)
+    cfg = _cfg(qk_nope_head_dim=nope, v_head_dim=vd, q_lora_rank=ql, hidden=hidden, heads=heads)
+    return cfg, q_b, kv_b, o
+
+
+def test_absorb_q_is_thread_count_invariant_and_equals_oracle(monkeypatch):
+    cfg, q_b, kv_b, _ = _absorb_case(1)
+    H = 3
+    ref = oracle.absorb_q(q_b, kv_b, heads=H, nope=8, rope=0, vd=6, kvl=512, ql=24)
+    rows = H * 512
+    for t in (1, 2, 3, 7, 64, rows, rows + 5):
+        got = dsa.absorb_q(cfg, q_b, kv_b, full_heads=H, threads=t)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), t
+    for env in ("5", " 3 ", "0", "-2", "abc", ""):
+        monkeypatch.setenv("DSA_ABSORB_THREADS", env)
+        got = dsa.absorb_q(cfg, q_b, kv_b, full_heads=H, threads=0)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), env
+
+
+def test_absorb_o_is_thread_count_invariant_and_equals_oracle():
+    cfg, _, kv_b, o = _absorb_case(2)
+    ref = oracle.absorb_o(o, kv_b, heads=3, nope=8, rope=0, vd=6, kvl=512, hidden=10)
+    for t in (1, 2, 4, 10, 0):
+        got = dsa.absorb_o(cfg, o, kv_b, local_heads=3, threads=t)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), t
+
+
+def test_absorb_refusals():
+    cfg, q_b, kv_b, o = _absorb_case(3)
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.absorb_q(cfg, q_b[:-1], kv_b, full_heads=3)
+    assert e.value.code == -11
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.absorb_q(cfg, q_b, kv_b[:-1], full_heads=3)
+    assert e.value.code == -11
+    rope = _cfg(qk_nope_head_dim=8, v_head_dim=6, q_lora_rank=24, hidden=10, heads=3,
+                qk_rope_head_dim=2)
+    qr = np.zeros((3 * 10, 24), np.float32)
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.absorb_q(rope, qr, kv_b, full_heads=3)
+    assert e.value.code == -10
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.absorb_o(rope, o, kv_b, local_heads=3)
+    assert e.value.code == -10
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.absorb_o(cfg, o[:, :-1], kv_b, local_heads=3)
+    assert e.value.code == -11
+
+
+def test_bf16_rounding_matches_oracle_and_generator():
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal(4096) * np.exp2(rng.integers(-30, 30, 4096))).astype(np.float32)
+    x[:4] = [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -0.0, 65504.0]
+    got = dsa.f32_to_bf16_rne(x)
+    assert np.array_equal(got, synth.bf16_bits(x))
+    assert all(int(got[i]) == oracle.bf16_from_float(float(x[i])) for i in range(0, 4096, 37))
+    assert got[0] == 0x3F80 and got[1] == 0x3F82
+
+
+# ---------------------------------------------------------------- refusals, no launch
+
+_NULL = None
+_FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below is refused first
+
+
+def test_refusals_return_codes_without_launching():
+    L = dsa.lib()
+    cfg = _cfg()
+    c = ctypes.byref(cfg)
+    bad = _cfg(index_kpool=9, index_topk=9)
+    # config rules reach every call
+    assert L.dsa_index_scores(ctypes.byref(bad), 1, 1, 8, 0, 1.0, _FAKE, _FAKE, _FAKE, _FAKE,
+                              _FAKE, 0, _NULL, _FAKE, _FAKE, _FAKE, _FAKE, _NULL) == -6
+    # null buffers
+    assert L.dsa_index_scores(c, 1, 1, 8, 0, 1.0, _NULL, _FAKE, _FAKE, _FAKE, _FAKE, 0, _NULL,
+                              _FAKE, _FAKE, _FAKE, _FAKE, _NULL) == -1
+    assert "NULL" in dsa.last_error()
+    # fp8 keys without scales; bad dtype
+    assert L.dsa_index_scores(c, 1, 1, 8, 0, 1.0, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 2, _NULL,
+                              _FAKE, _FAKE, _FAKE, _FAKE, _NULL) == -1
+    assert L.dsa_index_scores(c, 1, 1, 8, 0, 1.0, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, 1, _NULL,
+                              _FAKE, _FAKE, _FAKE, _FAKE, _NULL) == -3
+    # unsupported indexer geometry
+    assert L.dsa_index_scores(ctypes.byref(_cfg(index_head_dim=48)), 1, 1, 8, 0, 1.0, _FAKE,
+                              _FAKE, _FAKE, _FAKE, _FAKE, 0, _NULL, _FAKE, _FAKE, _FAKE, _FAKE,
+                              _NULL) == -14
+    assert L.dsa_index_scores(ctypes.byref(_cfg(index_heads=33)), 1, 1, 8, 0, 1.0, _FAKE,
+                              _FAKE, _FAKE, _FAKE, _FAKE, 0, _NULL, _FAKE, _FAKE, _FAKE, _FAKE,
+                              _NULL) == -14
+    # misaligned data pointer
+    odd = ctypes.c_void_p(0x10002)
+    assert L.dsa_index_scores(c, 1, 1, 8, 0, 1.0, odd, _FAKE, _FAKE, _FAKE, _FAKE, 0, _NULL,
+                              _FAKE, _FAKE, _FAKE, _FAKE, _NULL) == -2
+    # top-k rows beyond the register budget
+    assert L.dsa_topk_pools(c, 1, 65537, _FAKE, _FAKE, _FAKE, _NULL) == -14
+    # expand: more pools than the index_topk budget
+    assert L.dsa_expand_selection(c, 1, 513, 1, 4096, 0, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE,
+                                  _NULL) == -2
+    # kpool_compress negative size / null
+    assert L.dsa_kpool_compress(c, 1, -1, 0, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE,
+                                _NULL) == -2
+    assert L.dsa_kpool_compress(c, 1, 64, 0, _NULL, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE,
+                                _NULL) == -1
+    # sparse MLA: missing workspace when the plan splits
+    need = L.dsa_sparse_mla_decode_workspace(c, 32, 4096)
+    assert need > 0
+    assert L.dsa_sparse_mla_decode(c, 32, 4096, 32, 0.0625, _FAKE, _FAKE, _FAKE, _FAKE, 0,
+                                   _NULL, 1 << 20, 131072, _NULL, 0, 64, _FAKE, _NULL, _NULL, 0,
+                                   _NULL) == -12
+    assert L.dsa_sparse_mla_decode(c, 32, 4096, 32, 0.0625, _FAKE, _FAKE, _FAKE, _FAKE, 2,
+                                   _NULL, 1 << 20, 131072, _NULL, 0, 64, _FAKE, _NULL, _FAKE,
+                                   need, _NULL) == -1
+    assert L.dsa_sparse_mla_decode(ctypes.byref(_cfg(kv_lora_rank=576)), 1, 8, 1, 0.0625, _FAKE,
+                                   _FAKE, _FAKE, _FAKE, 0, _NULL, 64, 64, _NULL, 0, 64, _FAKE,
+                                   _NULL, _NULL, 0, _NULL) == -8
+    # empty work is accepted and launches nothing
+    assert L.dsa_index_scores(c, 0, 1, 8, 0, 1.0, _NULL, _NULL, _NULL, _NULL, _NULL, 0, _NULL,
+                              _NULL, _NULL, _NULL, _NULL, _NULL) == 0
+    assert L.dsa_compact_pools(0, 8, _NULL, _NULL, _NULL, _NULL) == 0
