@@ -1,0 +1,387 @@
+"""Decode throughput of the pooled-key DSA path on one MI355X.
+
+One step = one pass of the decode chain over a batch: compact_pools -> index_scores ->
+topk_pools -> expand_selection -> sparse_mla_decode (every launch goes through the C ABI).
+Default workload: 32 decode queries at contexts log-uniform in [4K, 131,072] tokens,
+index_kpool 8, index_topk 4,096, fp8 pooled keys and fp8 paged 512-wide latent with per-row
+scales, 32 indexer heads x 128 and 32 MLA heads.
+
+Protocol: inputs are resident in HBM; R replicas of every per-step input (pooled keys and
+scales, validity, q, w, q_abs, latent cache, block tables) are cycled step by step so the
+distinct bytes touched exceed 1 GiB (four times the 256 MB Infinity Cache). Steps are
+recorded into HIP graphs and replayed; HIP events bracket exactly K steps. Each stage is
+also replayed alone (its own graph over the same replicas) and timed with events, which
+gives the per-launch duration used for the roofline of the dominant kernel. The CPU oracle
+is timed on a sample of the same batch.
+
+Prints one JSON line (see the keys at the end of main()).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+MALL_BYTES = 256 << 20         # Infinity Cache
+KERNEL_SOURCES = {
+    "index_scores": "index_scores.hip",
+    "sparse_mla_decode": "sparse_mla_decode.hip",
+    "topk_pools": "topk_pools.hip",
+    "compact_pools": "compact_pools.hip",
+    "expand_selection": "expand_selection.hip",
+    "kpool_compress": "kpool_compress.hip",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash(kernel: str) -> str:
+    path = os.path.join(ROOT, "dsa_pooled_key_amd", "csrc", KERNEL_SOURCES[kernel])
+    h = hashlib.sha256(open(path, "rb").read())
+    for dep in ("dsa_device.hpp",):
+        h.update(open(os.path.join(ROOT, "dsa_pooled_key_amd", "csrc", dep), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary of this kernel, if it was
+    taken on the current source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- algorithmic bytes
+
+def algorithmic_bytes(di, n_valid, n_tokens):
+    """Bytes the method must move per step, by stage (inputs once, outputs once)."""
+    wl = di.wl
+    Q, Hi, D, H, B, P, W = wl.Q, wl.index_heads, wl.index_dim, wl.heads, wl.B, wl.pools, wl.width
+    key_row = D + 4 if wl.key_fp8 else 2 * D
+    tok_row = 512 + 4 if wl.kv_fp8 else 2 * 512
+    valid_pools = int(np.sum(n_valid[di.row_seq]))
+    return {
+        "compact_pools": B * P + B * P * 4 + B * 4,
+        "index_scores": valid_pools * (key_row + 4) + Q * Hi * (2 * D + 4) + Q * P * 5,
+        "topk_pools": Q * P * 5 + Q * wl.kw * 4,
+        "expand_selection": Q * wl.kw * 4 + Q * W * 4,
+        "sparse_mla_decode": n_tokens * tok_row + Q * W * 4 + Q * H * 512 * 2 + Q * H * (512 + 1) * 4,
+        # the method's own bytes for the whole step (intermediates excluded)
+        "step": valid_pools * key_row + B * P + Q * Hi * (2 * D + 4) + n_tokens * tok_row
+                + Q * H * 512 * 2 + Q * H * 512 * 4 + Q * W * 4,
+    }
+
+
+# ---------------------------------------------------------------- GPU part
+
+def run_gpu(args):
+    import torch
+
+    from dsa_pooled_key_amd import binding as dsa
+    from dsa_pooled_key_amd import synth
+    from dsa_pooled_key_amd.pipeline import DecodeStep, DeviceDecodeInputs
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    di = synth.make_decode_inputs(args.workload, seed=args.seed)
+    wl = di.wl
+    log(f"inputs for {wl.name} drawn in {time.time() - t0:.1f}s; libdsa {dsa.version()}")
+    x0 = DeviceDecodeInputs.upload(di, dev)
+    probe = DecodeStep(wl, x0, di.scale, di.sm_scale)
+    probe.run()
+    torch.cuda.synchronize()
+    n_valid = probe.n_valid.cpu().numpy()
+    n_tokens = int((probe.token_ids >= 0).sum().item())
+    alg = algorithmic_bytes(di, n_valid, n_tokens)
+    touched = alg["step"]
+    reps = args.replicas or int(min(48, max(4, -(-4 * MALL_BYTES // touched))))
+    log(f"step touches {touched / 2**20:.1f} MiB of algorithmic bytes; {reps} replicas "
+        f"-> {reps * touched / 2**30:.2f} GiB distinct per cycle; {n_tokens} tokens attended")
+
+    def clone(x):
+        return DeviceDecodeInputs(**{k: (None if v is None else v.clone())
+                                     for k, v in x.__dict__.items()})
+
+    xs = [x0] + [clone(x0) for _ in range(reps - 1)]
+    steps = [DecodeStep(wl, x, di.scale, di.sm_scale) for x in xs]
+    for i in range(max(args.warmup, reps)):
+        steps[i % reps].run()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+
+    def graph_of(fns):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for f in fns:
+                f()
+        return g
+
+    g_cycle = graph_of([s.run for s in steps])
+    g_single = [graph_of([s.run]) for s in steps]
+    for i in range(args.warmup):
+        g_single[i % reps].replay()
+    torch.cuda.synchronize()
+
+    def timed(cycle_graph, single_graphs, k):
+        """Replay exactly k launches of the recorded work, rotating replicas; ms per one."""
+        full, rest = divmod(k, len(single_graphs))
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(full):
+            cycle_graph.replay()
+        for i in range(rest):
+            single_graphs[i].replay()
+        stop.record(stream)
+        stop.synchronize()
+        return start.elapsed_time(stop) / k
+
+    ms_step = timed(g_cycle, g_single, args.steps)
+    log(f"decode step: {ms_step * 1e3:.2f} us ({wl.Q / ms_step * 1e3:.0f} queries/s)")
+
+    # Per-stage durations: each stage alone, same replicas, same graph replay.
+    stage_fns = {
+        "compact_pools": lambda s: dsa.compact_pools(s.x.pool_valid, s.ids, s.n_valid),
+        "index_scores": lambda s: dsa.index_scores(
+            s.cfg, s.x.q, s.x.w, s.x.row_seq, s.x.row_pos, s.x.keys, s.ids, s.n_valid,
+            first_key=wl.first_key, scale=s.scale, key_scales=s.x.key_scales, scores=s.scores,
+            cand=s.cand),
+        "topk_pools": lambda s: dsa.topk_pools(s.cfg, s.scores, s.cand, s.sel),
+        "expand_selection": lambda s: dsa.expand_selection(
+            s.cfg, s.sel, s.x.row_seq, s.x.row_pos, s.x.valid, S=wl.S, first_key=wl.first_key,
+            token_ids=s.token_ids),
+        "sparse_mla_decode": lambda s: s.attend(),
+    }
+    stage_us = {}
+    for name, fn in stage_fns.items():
+        gc = graph_of([(lambda s=s: fn(s)) for s in steps])
+        gs = [graph_of([(lambda s=s: fn(s))]) for s in steps]
+        for g in gs:
+            g.replay()
+        stage_us[name] = timed(gc, gs, args.steps) * 1e3
+    log("stages (us): " + ", ".join(f"{k} {v:.2f}" for k, v in stage_us.items()))
+
+    # Context build rate: kpool_compress over a token cache of the same shape (own inputs).
+    ki = synth.make_kpool_inputs(args.workload, seed=args.seed, batch=args.kpool_batch)
+    k = torch.from_numpy(ki.k.view(np.int16)).to(dev).view(torch.bfloat16)
+    g_ = torch.from_numpy(ki.gate.view(np.int16)).to(dev).view(torch.bfloat16)
+    ape = torch.from_numpy(ki.ape).to(dev)
+    valid = torch.from_numpy(ki.valid).to(dev)
+    kb, S = k.shape[0], k.shape[1]
+    P = dsa.num_pools(S, wl.first_key, wl.kpool)
+    pk = torch.empty((kb, P, wl.index_dim), dtype=torch.bfloat16, device=dev)
+    pv = torch.empty((kb, P), dtype=torch.uint8, device=dev)
+    cfg = steps[0].cfg
+    kp_run = lambda: dsa.kpool_compress(cfg, k, g_, ape, valid, wl.first_key, pk, pv)  # noqa: E731
+    kp_run()
+    g_kp = graph_of([kp_run])
+    n_kp = max(5, args.steps // 10)
+    kp_us = timed(g_kp, [g_kp], n_kp) * 1e3
+    kp_tokens = kb * P * wl.kpool
+    kp_bytes = kp_tokens * (wl.index_dim * 4 + 1) + kb * P * (wl.index_dim * 2 + 1)
+    torch.cuda.set_stream(torch.cuda.default_stream())
+
+    return {
+        "di": di, "alg": alg, "ms_step": ms_step, "stage_us": stage_us, "reps": reps,
+        "n_tokens": n_tokens, "kpool": {"us": kp_us, "tokens": kp_tokens, "bytes": kp_bytes,
+                                        "batch": kb},
+    }
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def run_cpu_baseline(di, sample_every: int):
+    import oracle
+
+    wl = di.wl
+    rows = np.arange(0, wl.Q, sample_every)
+    t0 = time.perf_counter()
+    ids, nv = oracle.compact_pools(di.pool_valid)
+    rs, rc = oracle.index_scores(di.q[rows], di.w[rows], di.row_seq[rows], di.row_pos[rows],
+                                 di.keys, ids, nv, kpool=wl.kpool, first_key=wl.first_key,
+                                 scale=di.scale, key_scales=di.key_scales)
+    sel = oracle.topk_pools(rs, rc, wl.kw)
+    tok = oracle.expand_selection(sel, di.row_seq[rows], di.row_pos[rows], di.valid,
+                                  kpool=wl.kpool, index_topk=wl.topk, always_select_tail=wl.tail,
+                                  first_key=wl.first_key)
+    oracle.sparse_mla(di.q_abs[rows], tok, di.row_seq[rows], di.kv, sm_scale=di.sm_scale,
+                      S=wl.S, kv_scales=di.kv_scales, block_table=di.block_table)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "queries/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(rows)} of the {wl.Q} queries of one step (every {sample_every}th), "
+                      f"whole decode chain, {dt:.1f} s wall"}
+
+
+# ---------------------------------------------------------------- main
+
+def run_eager(args):
+    """Profiling mode: the decode step launched eagerly (no graphs) over rotating replicas,
+    optionally one stage only, so counter runs see plain dispatches."""
+    import torch
+
+    from dsa_pooled_key_amd import binding as dsa
+    from dsa_pooled_key_amd import synth
+    from dsa_pooled_key_amd.pipeline import DecodeStep, DeviceDecodeInputs
+
+    di = synth.make_decode_inputs(args.workload, seed=args.seed)
+    wl = di.wl
+    x0 = DeviceDecodeInputs.upload(di, torch.device("cuda:0"))
+    reps = args.replicas or 4
+    xs = [x0] + [DeviceDecodeInputs(**{k: (None if v is None else v.clone())
+                                       for k, v in x0.__dict__.items()}) for _ in range(reps - 1)]
+    steps = [DecodeStep(wl, x, di.scale, di.sm_scale) for x in xs]
+    for s in steps:
+        s.run()
+    torch.cuda.synchronize()
+    fn = {"all": lambda s: s.run(), "select": lambda s: s.select(),
+          "attend": lambda s: s.attend()}[args.eager]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fn(steps[i % reps])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    print(json.dumps({"mode": f"eager:{args.eager}", "workload": wl.name, "steps": args.steps,
+                      "replicas": reps, "wall_ms_per_step": dt / args.steps * 1e3,
+                      "libdsa": dsa.version()}), flush=True)
+
+
+def run_copy_calibration(args):
+    """A plain device copy of a known size, for scaling the FETCH_SIZE / WRITE_SIZE
+    counters: each launch reads and writes exactly `bytes`."""
+    import torch
+
+    n = args.copy_bytes
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy_calibration", "bytes_per_launch": n, "launches": args.steps}),
+          flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="fp8_mixed_b32")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--replicas", type=int, default=0)
+    ap.add_argument("--kpool-batch", type=int, default=8)
+    ap.add_argument("--cpu-sample-every", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", choices=["all", "select", "attend"], default=None,
+                    help="profiling mode: eager launches only, no timing report")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="profiling mode: plain copies of --copy-bytes for counter scaling")
+    ap.add_argument("--copy-bytes", type=int, default=256 << 20)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        raise SystemExit(2)
+    if args.copy_calibration:
+        return run_copy_calibration(args)
+    if args.eager:
+        return run_eager(args)
+
+    res = run_gpu(args)
+    di, alg, ms = res["di"], res["alg"], res["ms_step"]
+    wl = di.wl
+    value = wl.Q / (ms * 1e-3)
+
+    # Dominant kernel: the stage with the largest share of the step.
+    dom = max(("index_scores", "sparse_mla_decode", "topk_pools"), key=lambda k: res["stage_us"][k])
+    dom_us = res["stage_us"][dom]
+    achieved = alg[dom] / (dom_us * 1e-6) / 1e9
+    traffic = measured_traffic(dom, wl.name)
+    step_gbs = alg["step"] / (ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        cpu = run_cpu_baseline(di, args.cpu_sample_every)
+
+    kp = res["kpool"]
+    line = {
+        "metric": "DSA decode queries/s (index+topk+sparse MLA) at 128K ctx; % peak HBM GB/s",
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8(e4m3)->bf16 mfma, f32 accumulate" if wl.kv_fp8 else "bf16 mfma, f32 accumulate",
+        "data": "synthetic (seeded generators; no dataset or trained weights)",
+        "config": {
+            "workload": f"{wl.name}: {wl.Q} decode queries, contexts log-uniform in [4096, {wl.S}], "
+                        f"kpool {wl.kpool}, topk {wl.topk}, indexer {wl.index_heads}x{wl.index_dim} "
+                        f"{'fp8' if wl.key_fp8 else 'bf16'} keys, MLA {wl.heads} heads x 512 "
+                        f"{'fp8' if wl.kv_fp8 else 'bf16'} latent, "
+                        f"{'paged 64-token blocks' if wl.paged else 'contiguous'}",
+            "global_batch": wl.Q,
+            "seq_len": wl.S,
+            "parallelism": "single GPU",
+            "replicas": res["reps"],
+            "tokens_attended_per_step": res["n_tokens"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg[dom],
+            "launch_us": round(dom_us, 3),
+        },
+        "step_roofline": {
+            "algorithmic_bytes": alg["step"],
+            "achieved_GBs": round(step_gbs, 1),
+            "frac_of_peak_hbm": round(step_gbs / PEAK_HBM_GBS, 4),
+        },
+        "stage_us": {k: round(v, 3) for k, v in res["stage_us"].items()},
+        "kpool_compress": {
+            "tokens_per_s": round(kp["tokens"] / (kp["us"] * 1e-6), 1),
+            "launch_us": round(kp["us"], 2),
+            "achieved_GBs": round(kp["bytes"] / (kp["us"] * 1e-6) / 1e9, 1),
+            "frac_of_peak_hbm": round(kp["bytes"] / (kp["us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "sequences": kp["batch"],
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

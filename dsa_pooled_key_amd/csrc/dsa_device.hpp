@@ -27,8 +27,10 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return bf16_rne(lo) | (bf16_rne(hi) << 16);
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Four OCP e4m3 codes (one dword) -> four bf16 (two dwords). Exact: every e4m3 value is a
@@ -43,6 +45,28 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t codes) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+typedef short __attribute__((ext_vector_type(4))) i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// gfx950 LDS transpose read of 16-bit elements (ds_read_b64_tr_b16). Each lane addresses
+// 8 bytes (4 elements) of LDS; within every group of 16 lanes, result lane i, element e is
+// element i%4 of the 8 bytes addressed by lane 4*e + i/4 of the same group.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t *lds_ptr) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(lds_ptr));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+typedef int __attribute__((ext_vector_type(2))) i32x2;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// gfx950 LDS transpose read of 8-bit elements (ds_read_b64_tr_b8). Each lane addresses
+// 8 bytes; within every group of 16 lanes, result lane i, byte e is byte i%8 of the 8 bytes
+// addressed by lane 2*e + i/8 of the same group.
+__device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t *lds_ptr) {
+    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)(lds_ptr));
+    return __builtin_bit_cast(u32x2, v);
+}
 
 // e^x through the hardware base-2 exponential.
 __device__ __forceinline__ float fast_exp(float x) {
