@@ -231,7 +231,7 @@ int dsa_expand_selection(const dsa_config *cfg, int Q, int Kw, int B, int S, int
 
 size_t dsa_sparse_mla_decode_workspace(const dsa_config *cfg, int Q, int W) {
     clear_error();
-    if (check_config(cfg) || Q < 0 || W < 0) return 0;
+    if (check_config(cfg) || Q < 0 || W < 0 || W > DSA_MAX_MLA_WIDTH) return 0;
     return dsa::plan_sparse_mla(Q, W, cfg->heads).ws_bytes;
 }
 
@@ -247,6 +247,10 @@ int dsa_sparse_mla_decode(const dsa_config *cfg, int Q, int W, int B, float sm_s
     if (Q < 0 || W < 0 || B < 0 || S < 0 || kv_rows < 0) return set_error(DSA_ERR_BAD_SIZE, "negative size");
     if (kv_dtype != DSA_BF16 && kv_dtype != DSA_FP8_E4M3)
         return set_error(DSA_ERR_BAD_DTYPE, "sparse_mla_decode: latent must be bf16 or fp8 e4m3");
+    if (kv_rows > INT32_MAX)
+        return set_error(DSA_ERR_UNSUPPORTED, "sparse_mla_decode: kv_rows above 2^31 - 1");
+    if (W > DSA_MAX_MLA_WIDTH)
+        return set_error(DSA_ERR_UNSUPPORTED, "sparse_mla_decode: W = %d above %d", W, DSA_MAX_MLA_WIDTH);
     if (Q == 0) return DSA_OK;
     const bool fp8 = kv_dtype == DSA_FP8_E4M3;
     if (!q_abs || !row_seq || !out || (W > 0 && !token_ids))

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "dsa.h"
+
 namespace dsa {
 
 hipError_t launch_kpool_compress(int B, int S, int D, int KP, int first_key, int P,
@@ -32,6 +34,11 @@ hipError_t launch_expand_selection(int Q, int Kw, int KP, int topk, int W, bool 
                                    int S, int first_key, int P, const int32_t *sel,
                                    const int32_t *row_seq, const int32_t *row_pos,
                                    const uint8_t *valid, int32_t *token_ids, hipStream_t stream);
+
+// Sparse MLA split limits: token slots one block resolves up front, splits per row.
+constexpr int kMlaMaxSplit = 512;
+constexpr int kMlaMaxSplits = 64;
+static_assert(kMlaMaxSplit * kMlaMaxSplits >= DSA_MAX_MLA_WIDTH, "widest selection must fit");
 
 struct MlaPlan {
     int groups;      // 32-head groups

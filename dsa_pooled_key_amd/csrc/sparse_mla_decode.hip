@@ -5,22 +5,22 @@
 // attention restricted to the expanded token ids, and the serve path reads those tokens
 // through a block table with no sequence-length-sized buffer.
 //
-// Keys and values are the same latent rows, so each 32-token tile is gathered once from
-// HBM (bf16, or fp8 converted exactly to bf16 in registers), stored once in LDS as a
-// [token][channel] bf16 tile, and read by both products:
-//   S^T = K . Q^T  on v_mfma_f32_16x16x32_bf16: wave w computes 16 tokens x 16 heads over all
-//                  512 channels; its query fragment (64 registers) stays resident.
-//   O  += P . V    on v_mfma_f32_32x32x16_bf16: wave w owns 32 heads x 128 channels of the
-//                  output accumulator (64 registers) and reads P (bf16) from LDS and V down
-//                  the token axis of the same tile with gfx950's LDS transpose read.
-// The softmax is online (running max and sum per head). The two waves that score the same
-// 16 heads exchange their tile maxima through LDS; each keeps its own partial sum, combined
-// at the end. For fp8 the per-token scale multiplies the logit and the probability, so no
-// rounding beyond bf16 P is added.
+// Keys and values are the same latent rows, so each 32-token tile is gathered once from HBM
+// straight into LDS (global_load_lds, no registers) in its storage format -- fp8 e4m3 rows of
+// 512 bytes or bf16 rows of 1 KiB -- and read there by both products:
+//   S^T = K . Q^T  on v_mfma_f32_16x16x32_bf16: wave w scores 16 tokens x 16 heads over all 512
+//                  channels; its query fragment (64 registers) stays resident. fp8 rows are
+//                  read 16 channels at a time and converted to bf16 in registers (exact).
+//   O  += P . V    on v_mfma_f32_32x32x16_bf16: wave w owns 32 heads x 128 channels of the output
+//                  accumulator (64 registers), reads P (bf16) from LDS and V down the token axis
+//                  of the same tile with gfx950's LDS transpose reads (8-bit for fp8 rows, then
+//                  converted; 16-bit for bf16 rows).
+// The softmax is online with a lazily moved reference maximum per head. For fp8 the per-token
+// scale multiplies the logit and the probability, so no rounding beyond bf16 P is added.
 //
-// Split over tokens: block (r, s, g) takes token slots [s*L, s*L + L) of row r for head group
-// g. With one split the block writes out and lse directly; with several it writes
-// (max, sum, unnormalised O) to the workspace and mla_combine merges them.
+// Split over tokens: block (r, s, g) takes token slots [s*L, s*L + L) of row r for head group g.
+// With one split the block writes out and lse directly; with several it writes (max, sum,
+// unnormalised O) to the workspace and mla_combine merges them.
 //
 // Bytes per selected token: 1024 (bf16) or 516 (fp8 + scale) of latent, 4 of token id.
 #include "dsa_device.hpp"
@@ -31,38 +31,58 @@ namespace {
 
 constexpr int kC = 512;
 constexpr int kTile = 32;
-constexpr int kThreads = 512;          // 8 waves: two teams of 4 on alternate tiles
-constexpr int kMaxSplit = 1024;        // token slots one block resolves up front
-constexpr int kMaxSplits = 64;         // splits per (row, group)
-constexpr int kPStride = kTile + 8;    // bf16 per P row
-constexpr int kPartFloats = 64 + 32 * kC;  // per (row, group, split): max[32], sum[32], O[32][512]
+constexpr int kThreads = 256;          // 4 waves
+constexpr int kMaxSplit = kMlaMaxSplit;   // token slots one block resolves up front
+constexpr int kMaxSplits = kMlaMaxSplits; // splits per (row, group)
+constexpr int kPStride = kTile + 8;    // bf16 per P row (80 bytes: conflict-free row reads)
+// Split partial per (row, group, split): max[32] and sum[32] (f32), then the unnormalised O of
+// 32 heads x 512 channels in bf16 -- the precision of the P operand it was accumulated from --
+// stored in accumulator order: 16-byte vector ((v*4 + nt)*2 + i8)*64 + lane holds
+// acc[nt][8*i8 .. 8*i8 + 7] of lane `lane` of wave v.
+constexpr int kPartHeader = 256;
+constexpr int kPartBytes = kPartHeader + 32 * kC * 2;
 
-// Tiles of 32 latent rows. The working tile is bf16, one 1 KiB row per token, its 16-byte
-// chunks XOR-swizzled (chunk c of row r at position c ^ swz_work(r)) so that the QK operand
-// reads (16 rows, one chunk column) and the transposing V reads (4 rows, 4 chunk columns per
-// 32 lanes) each touch distinct LDS banks. Rows arrive by global_load_lds_dwordx4 (16 bytes
-// a lane, no registers): a bf16 latent lands directly in a ring of working tiles; an fp8
-// latent lands in a ring of raw 512-byte rows (chunk c of row r at c ^ 8*(r&1)) and the
-// wave that fetched a row converts it into the working tile, once per element.
-__device__ __forceinline__ int swz_work(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
-constexpr int kWorkRow = 1024;
-constexpr int kWorkTile = kTile * kWorkRow;
-constexpr int kRawRow = 512;
-constexpr int kRawWave = 8 * kRawRow;  // the 8 rows of one tile one wave fetches
+// Tile geometry per storage format. A tile is 32 rows; rows arrive by 16-byte-a-lane DMA and
+// keep their storage format in LDS. Chunk c (16 bytes) of row r sits at position c ^ swz(r);
+// the two swizzles were chosen by measuring each read pattern below on gfx950 (all four run
+// at the conflict-free rate of their instruction).
+template <bool FP8>
+struct Geo {
+    static constexpr int kRowBytes = FP8 ? 512 : 1024;
+    static constexpr int kTileBytes = kTile * kRowBytes;
+    static constexpr int kStages = FP8 ? 4 : 2;            // tiles resident in the ring
+    static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows one wave-wide load covers
+    static constexpr int kLoads = 8 / kRowsPerLoad;        // row loads per wave per tile (8 rows)
+    static constexpr int kLoadsT = kLoads + (FP8 ? 1 : 0); // plus the rows' fp8 scales
+    static constexpr int kLanesPerRow = kWave / kRowsPerLoad;
+};
+template <bool FP8>
+__device__ __forceinline__ int swz(int r) {
+    return FP8 ? ((r & 15) ^ ((r >> 4) & 1)) : (((r & 7) << 1) | ((r >> 3) & 1));
+}
 // The softmax keeps a reference maximum per head and moves it only when a tile's maximum
 // exceeds it by more than this many (natural-log) units, so the accumulator is rescaled on
 // few tiles; unnormalised weights stay below e^8.
 constexpr float kRescaleSlack = 8.0f;
 
 // One 16-byte-a-lane global -> LDS copy (global_load_lds_dwordx4): lane l's 16 bytes land
-// at lds_base + 16*l. Issued as inline assembly so the compiler does not treat it as an LDS
-// write and order every later LDS read behind it; completion is tracked by the explicit
-// vmcnt waits below (loads complete in order, so the compiler's own waits stay correct).
+// at lds_base + 16*l. Issued as inline assembly without a memory clobber, so the compiler
+// neither orders nearby LDS reads behind it nor waits for it: it only writes a stage that no
+// code reads before the explicit vmcnt wait and block barrier that publish it (loads complete
+// in order, so the compiler's own waits for other loads stay correct).
 __device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
                  : "s"(lds_base), "v"(src)
-                 : "memory", "m0");
+                 : "m0");
+}
+
+// Same for 4 bytes a lane (global_load_lds_dword): lane l's dword lands at lds_base + 4*l.
+__device__ __forceinline__ void dma4(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :
+                 : "s"(lds_base), "v"(src)
+                 : "m0");
 }
 
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
@@ -89,11 +109,18 @@ __device__ __forceinline__ T lds_load(const uint8_t *base, uint32_t off) {
     return *reinterpret_cast<const T *>(base + off);
 }
 
-// Block = 8 waves in two teams. Team tm (waves 4tm..4tm+3) processes tiles tm, tm+2, ...
-// with its own working tile, P tile and softmax state; all waves share the barriers, so the
-// two teams advance in lockstep, each barrier covering two tiles. At the end the teams'
-// (max, sum, O) are merged through LDS. Within a team, wave v (0..3) scores tile rows
-// 16*(v>>1).. x heads 16*(v&1).. and accumulates O for channels 128v..128v+127.
+// Four e4m3 codes -> four bf16 and eight -> eight (exact).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+    const u32x2 a = e4m3x4_to_bf16x4(lo), b = e4m3x4_to_bf16x4(hi);
+    return u32x4{a.x, a.y, b.x, b.y};
+}
+
+// Block = 4 waves. Wave v scores tile rows 16*(v>>1).. x heads 16*(v&1).. and accumulates O
+// for channels 128v..128v+127 of all 32 heads of group g.
+//
+// Query channels are permuted inside each MFMA step (the contraction order is free as long
+// as both operands agree): step s, lane group k (= lane>>4) covers channels
+// 64*(s>>1) + 16k + 8*(s&1) .. +7, so one 16-byte read of an fp8 row feeds two steps.
 template <bool FP8, bool PAGED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void sparse_mla_kernel(
     int W, int H, int B, int splits, int split_len, float sm_scale,
@@ -102,25 +129,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const float *__restrict__ kv_scales, long long kv_rows, int S,
     const int32_t *__restrict__ block_table, int max_blocks, int block_size,
     float *__restrict__ out, float *__restrict__ lse, float *__restrict__ ws) {
-    // fp8: a private raw ring per wave (2 stages x 8 rows) + one working tile per team.
-    // bf16: a ring of 2 working tiles per team.
-    constexpr int kRingBytes = FP8 ? (8 * 2 * kRawWave + 2 * kWorkTile) : 4 * kWorkTile;
-    constexpr int kRowBytes = FP8 ? kRawRow : kWorkRow;   // bytes a fetched row takes
-    constexpr int kRowsPerLoad = 1024 / kRowBytes;         // rows per 64-lane 16-byte load
-    constexpr int kLoadsPerWave = 8 / kRowsPerLoad;        // per wave per tile
-    constexpr int kLanesPerRow = kWave / kRowsPerLoad;
-    static_assert(kRingBytes >= 2 * 32 * kC * 4 / 2, "merge area fits in the ring");
+    using G_ = Geo<FP8>;
+    constexpr int NS = G_::kStages;
+    constexpr int RB = G_::kRowBytes;
 
-    __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
-    __shared__ __attribute__((aligned(16))) uint16_t pl[2][32 * kPStride];
-    __shared__ int rows_s[kMaxSplit];
-    __shared__ float scale_s[kMaxSplit];
-    __shared__ float red[8][16];
-    __shared__ float alpha_s[2][32];
-    __shared__ float msum_s[2][32];
-    __shared__ float lsum_s[2][32];
-    __shared__ int last_s;
-    __shared__ int rescale_s[2][2];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NS * G_::kTileBytes];
+    __shared__ __attribute__((aligned(16))) uint16_t pl[32 * kPStride];
+    __shared__ __attribute__((aligned(16))) int rows_s[kMaxSplit];
+    // fp8 scales of each resident tile: wave w's 8 rows at [stage][w][0..7] (64 per wave land).
+    __shared__ __attribute__((aligned(16))) float sc_ring[FP8 ? NS : 1][4][kWave];
+    __shared__ float red[4][16];
+    __shared__ float alpha_s[32];
+    __shared__ float msum_s[32];
+    __shared__ float lsum_s[32];
+    __shared__ int last_w[4];
+    __shared__ int rescale_s[2];
 
     const int r = blockIdx.x;
     const int split = blockIdx.y;
@@ -128,298 +151,320 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int G = gridDim.z;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;       // 0..7
-    const int tm = wave >> 2;           // team
-    const int v = wave & 3;             // wave within the team
+    const int v = tid / kWave;  // wave 0..3
+    const int lg = lane >> 4;   // 16-lane group
     const int b = row_seq[r];
     const bool row_ok = b >= 0 && b < B;
     const int s0 = split * split_len;
     const int n_slots = max(0, min(split_len, W - s0));
     const uint8_t *kvb = static_cast<const uint8_t *>(kv);
 
-    // Query fragment for S^T = K Q^T (B operand): head column lane&15 of this wave's 16,
-    // channels 32*st + (lane>>4)*8 .. +8 at step st. Issued first; used after the prologue.
+    // The block's 32 query rows (1 KiB each) are staged once through LDS, in the upper half of
+    // the ring, which no tile uses before every wave has taken its fragment: wave v fetches
+    // heads 8v..8v+7, chunk c of head row h at position c ^ swz<false>(h).
+    uint8_t *const qlds = ring + 32768;
     const int qk_head_local = 16 * (v & 1) + (lane & 15);
     const int qk_head = g * 32 + qk_head_local;
-    u32x4 qf[16];
 #pragma unroll
-    for (int st = 0; st < 16; ++st) {
-        qf[st] = u32x4{0u, 0u, 0u, 0u};
-        if (qk_head < H)
-            qf[st] = *reinterpret_cast<const u32x4 *>(q_abs + ((size_t)r * H + qk_head) * kC +
-                                                      32 * st + (lane >> 4) * 8);
+    for (int k = 0; k < 8; ++k) {
+        const int hl = 8 * v + k;
+        if (g * 32 + hl < H)
+            dma16(reinterpret_cast<const uint8_t *>(q_abs + ((size_t)r * H + g * 32 + hl) * kC) +
+                      16 * (lane ^ swz<false>(hl)),
+                  __builtin_amdgcn_readfirstlane(lds_offset(qlds + hl * 1024)));
     }
 
-    // ---- prologue: resolve every slot of the split to a latent row (or -1) and its scale
-    if (tid == 0) last_s = -1;
-    if (tid < 4) rescale_s[tid >> 1][tid & 1] = 0;
-    __syncthreads();
-    int my_last = -1;
-    for (int i = tid; i < n_slots; i += kThreads) {
-        const int tok = token_ids[(size_t)r * W + s0 + i];
-        long long row = -1;
-        if (tok >= 0 && row_ok && (S <= 0 || tok < S)) {
-            if constexpr (PAGED) {
-                const int blk = tok / block_size;
-                if (blk < max_blocks) {
-                    const int pb = block_table[(size_t)b * max_blocks + blk];
-                    if (pb >= 0) row = (long long)pb * block_size + (tok - blk * block_size);
-                }
-            } else {
-                row = (long long)b * S + tok;
-            }
-            if (row >= kv_rows) row = -1;
-        }
-        float sc = 1.0f;
-        if constexpr (FP8) sc = row >= 0 ? kv_scales[row] : 0.0f;
-        rows_s[i] = (int)row;
-        scale_s[i] = sc;
-        if (row >= 0) my_last = i;
-    }
-    if (my_last >= 0) atomicMax(&last_s, my_last);
-    wait_vm<0>();  // the query fragment is in registers before any tile load is issued
-    __syncthreads();
-    const int n_tiles = (last_s + kTile) / kTile;  // through the last slot with a token
-    const int n_iter = (n_tiles + 1) / 2;           // tile pairs
-
-    // ---- LDS addressing, hoisted out of the tile loop (all offsets are per lane).
-    uint8_t *const work0 = FP8 ? ring + 8 * 2 * kRawWave + tm * kWorkTile : ring + 2 * tm * kWorkTile;
-    // fetch: wave v fetches rows 8v..8v+7 of its team's tiles; a slot without a token fetches
-    // latent row 0 (finite data; its weight is zero). fp8 rows go to the wave's own raw ring.
-    auto stage_of = [&](int t) -> uint8_t * {   // where tile t's fetched rows of this wave go
-        const int st2 = (t >> 1) & 1;
-        if constexpr (FP8) return ring + (wave * 2 + st2) * kRawWave;
-        else return ring + (2 * tm + st2) * kWorkTile + 8 * v * kWorkRow;
-    };
+    // ---- DMA: wave v fetches rows 8v..8v+7 of every tile (and, for fp8, their scales). A slot
+    // without a token fetches latent row 0 (finite data; its weight is zero).
+    const int dma_rl = lane / G_::kLanesPerRow;                    // row within one load
+    const uint32_t dma_col = 16 * ((lane % G_::kLanesPerRow));     // byte position in the row
     auto issue = [&](int t) {
-        uint8_t *stage = stage_of(t);
+        uint8_t *stage = ring + (t % NS) * G_::kTileBytes + 8 * v * RB;
+        const int4 ra = *reinterpret_cast<const int4 *>(rows_s + t * kTile + 8 * v);
+        const int4 rb = *reinterpret_cast<const int4 *>(rows_s + t * kTile + 8 * v + 4);
+        const int rws[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
 #pragma unroll
-        for (int k = 0; k < kLoadsPerWave; ++k) {
-            const int rl = k * kRowsPerLoad + lane / kLanesPerRow;  // row within the wave's 8
-            const int rr = 8 * v + rl;                              // row within the tile
-            const int pos = lane % kLanesPerRow;
-            const int slot = t * kTile + rr;
-            int prow = slot < n_slots ? rows_s[slot] : -1;
-            if (prow < 0) prow = 0;
-            const int chunk = FP8 ? (pos ^ (8 * (rr & 1))) : (pos ^ swz_work(rr));
-            const uint8_t *src = kvb + (size_t)prow * kRowBytes + 16 * chunk;
-            dma16(src, __builtin_amdgcn_readfirstlane(
-                           lds_offset(stage + k * kRowsPerLoad * kRowBytes)));
+        for (int k = 0; k < G_::kLoads; ++k) {
+            const int rl = k * G_::kRowsPerLoad;  // first row of this load within the wave's 8
+            int prow = G_::kRowsPerLoad == 2 ? (dma_rl ? rws[rl + 1] : rws[rl]) : rws[rl];
+            prow = max(prow, 0);
+            const int rr = 8 * v + rl + dma_rl;  // row within the tile
+            const uint8_t *src = kvb + (size_t)prow * RB + (dma_col ^ (uint32_t)(16 * swz<FP8>(rr)));
+            dma16(src, __builtin_amdgcn_readfirstlane(lds_offset(stage + k * 1024)));
+        }
+        if constexpr (FP8) {
+            const int srow = max(rows_s[t * kTile + 8 * v + (lane & 7)], 0);
+            dma4(kv_scales + srow, __builtin_amdgcn_readfirstlane(lds_offset(&sc_ring[t % NS][v][0])));
         }
     };
-    // fp8 conversion: lane -> row 8v + lane/8, raw chunks (lane&7) + 8k, k = 0..3.
-    const int cv_row = 8 * v + (lane >> 3);
-    const uint32_t cv_raw = (uint32_t)((lane >> 3) * kRawRow + 16 * (lane & 7));
-    const int cv_flip = 8 * (cv_row & 1) * 16;  // raw chunk c sits at c ^ 8(r&1): 128-byte swap
-    const int cv_sw = swz_work(cv_row);
-    const uint32_t cv_w0 = (uint32_t)(cv_row * kWorkRow + 16 * ((2 * (lane & 7)) ^ cv_sw));
-    const uint32_t cv_w1 = (uint32_t)(cv_row * kWorkRow + 16 * ((2 * (lane & 7) + 1) ^ cv_sw));
-    // QK operand: row tb + (lane&15), chunk 4*st + (lane>>4) at position ^ swz_work(row):
-    // offset = row*1024 + 64*(st ^ kq) + 16*lq with kq, lq from the row's swizzle.
+
+    // ---- prologue: wave v resolves the slots its own DMA fetches -- slot t*32 + 8v + j of
+    // every tile t -- to latent rows (or -1) and issues the first tiles at once; it reads
+    // back only the entries it wrote, so no barrier precedes the loads. Slots past n_slots up
+    // to the tile boundary read as "no token", so the tile loop needs no bounds test.
+    const int n_ptiles = (n_slots + kTile - 1) / kTile;
+    int my_last = -1;
+    for (int t0 = 0; t0 < n_ptiles; t0 += 8) {
+        const int t = t0 + (lane >> 3);
+        if (t < n_ptiles) {
+            const int i = t * kTile + 8 * v + (lane & 7);
+            const int tok = i < n_slots ? token_ids[(size_t)r * W + s0 + i] : -1;
+            long long row = -1;
+            if (tok >= 0 && row_ok && (S <= 0 || tok < S)) {
+                if constexpr (PAGED) {
+                    const int blk = tok / block_size;
+                    if (blk < max_blocks) {
+                        const int pb = block_table[(size_t)b * max_blocks + blk];
+                        if (pb >= 0) row = (long long)pb * block_size + (tok - blk * block_size);
+                    }
+                } else {
+                    row = (long long)b * S + tok;
+                }
+                if (row >= kv_rows) row = -1;
+            }
+            rows_s[i] = (int)row;
+            if (row >= 0) my_last = i;
+        }
+    }
+    // Tiles issued ahead: fp8 keeps two tiles in flight beyond the one being scored (a fourth
+    // stage holds the tile whose products are still pending); bf16 keeps one tile in flight
+    // and refills after the barrier that opens tile t. A tile without tokens fetches row 0,
+    // so nothing is fetched from an empty latent buffer.
+    const int pre = kv_rows > 0 ? min(n_ptiles, FP8 ? 2 : 1) : 0;
+    for (int t = 0; t < pre; ++t) issue(t);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) my_last = max(my_last, __shfl_xor(my_last, d, kWave));
+    if (lane == 0) last_w[v] = my_last;
+    if (tid < 2) rescale_s[tid] = 0;
+    // The query rows, ids and table entries have landed (loads complete in order); fp8 also
+    // waits for its own rows of tile 0. The barrier publishes both.
+    if (FP8 && pre == 2) wait_vm<G_::kLoadsT>();
+    else if (FP8 || pre == 0) wait_vm<0>();
+    else wait_vm<G_::kLoadsT>();
+    __syncthreads();
+    const int last = max(max(last_w[0], last_w[1]), max(last_w[2], last_w[3]));
+    const int n_tiles = (last + kTile) / kTile;  // through the last slot with a token
+
+    // Query fragment for S^T = K Q^T (B operand): head column lane&15 of this wave's 16; step st,
+    // lane group lg holds channels 64(st>>1) + 16lg + 8(st&1) .. +7 (chunk 8(st>>1) + 2lg + (st&1)).
+    u32x4 qf[16];
+    {
+        const int sw = swz<false>(qk_head_local);
+#pragma unroll
+        for (int st = 0; st < 16; ++st) {
+            const int c = 8 * (st >> 1) + 2 * lg + (st & 1);
+            qf[st] = qk_head < H ? lds_load<u32x4>(qlds, (uint32_t)(qk_head_local * 1024 + 16 * (c ^ sw)))
+                                 : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    // ---- LDS read offsets, hoisted out of the tile loop (per lane, within one tile).
+    // QK operand: row tb + (lane&15). fp8: read jj (0..7) takes chunk 4jj + lg (two steps);
+    // bf16: step st takes chunk 8(st>>1) + 2lg + (st&1). Both: base + 64/256 * (...) forms.
     const int tb = 16 * (v >> 1);
     const int qk_row = tb + (lane & 15);
-    const int qk_sw = swz_work(qk_row);
-    const uint32_t qk_base = (uint32_t)(qk_row * kWorkRow + 16 * (((lane >> 4) ^ qk_sw) & 3));
-    const int qk_k = qk_sw >> 2;
+    const int qk_sw = swz<FP8>(qk_row);
     uint32_t qk_off[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qk_off[j] = qk_base + 64 * (j ^ qk_k);
-    // V operand (two transpose reads per fragment): source lane src of 16-lane group grp reads
-    // row 16*ks + 8*(grp>>1) + (src>>2) (+4), 4 channels at 128v + 32nt + 16(grp&1) + 4(src&3).
-    const int grp = lane >> 4, src = lane & 15;
-    const int va = src >> 2;                    // row & 3, equal for both reads
-    const int vb = 2 * (grp >> 1);              // (row >> 2) & 3 of the first read
-    const int ve = 2 * (grp & 1) + ((src & 3) >> 1);
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (FP8)  // chunk 4jj + lg, jj = 4a + j: position 16a + 4(j ^ sw>>2) + (lg ^ sw&3)
+            qk_off[j] = (uint32_t)(qk_row * RB + 16 * (4 * (j ^ (qk_sw >> 2)) + (lg ^ (qk_sw & 3))));
+        else  // chunk 8(st>>1) + 2lg + (st&1), st = 4a + j: position 16a + ((8(j>>1) + 2lg + (j&1)) ^ sw)
+            qk_off[j] = (uint32_t)(qk_row * RB + 16 * ((8 * (j >> 1) + 2 * lg + (j & 1)) ^ qk_sw));
+    }
+    // V operand. fp8 (one 8-bit transpose read per fragment): source lane s of group lg reads
+    // row 16ks + 8(lg>>1) + (s>>1), channels 128v + 32nt + 16(lg&1) + 8(s&1) .. +7.
+    // bf16 (two 16-bit transpose reads): row 16ks + 8(lg>>1) + (s>>2) + 4h, channels
+    // 128v + 32nt + 16(lg&1) + 4(s&3) .. +3.
+    const int vs = lane & 15;
     uint32_t v_off[2][4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-            v_off[h][nt] = (uint32_t)((8 * (grp >> 1) + va + 4 * h) * kWorkRow + 256 * v +
-                                      64 * (nt ^ va) + 16 * (ve ^ (vb + h)) + 8 * (src & 1));
+        for (int nt = 0; nt < 4; ++nt) {
+            if constexpr (FP8) {  // x = ks
+                const int row = 16 * x + 8 * (lg >> 1) + (vs >> 1);
+                const int c = 8 * v + 2 * nt + (lg & 1);
+                v_off[x][nt] = (uint32_t)(row * RB + 16 * (c ^ swz<true>(row)) + 8 * (vs & 1));
+            } else {  // x = h; ks adds 16 rows (same swizzle)
+                const int row = 8 * (lg >> 1) + (vs >> 2) + 4 * x;
+                const int ch = 128 * v + 32 * nt + 16 * (lg & 1) + 4 * (vs & 3);
+                v_off[x][nt] = (uint32_t)(row * RB + 16 * ((ch >> 3) ^ swz<false>(row)) + 2 * (ch & 7));
+            }
+        }
 
-    for (int t = tm; t < 2 && t < n_tiles; t += 2) issue(t);   // first tile of each team
-    if constexpr (FP8) {
-        if (tm + 2 < n_tiles) issue(tm + 2);                     // fp8: one more in flight
-    }
-
-    float m_ref = -INFINITY;  // reference maximum of head qk_head in this team
+    float m_ref = -INFINITY;  // reference maximum of head qk_head
     float l_run = 0.0f;       // this lane's share of the running sum
     f32x16 acc[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x16{};
 
-    for (int it = 0; it < n_iter; ++it) {
-        const int t = 2 * it + tm;          // this team's tile (may be past the end: idle)
-        const bool live = t < n_tiles;
-        const int par = it & 1;
-        uint8_t *Wt;
+    // ---- phases of one tile
+    // Scores S^T[token][head] for this wave's 16 tokens x 16 heads (two MFMA chains), scaled
+    // and masked into x; sc gets the rows' fp8 scales (1 for bf16, 0 where there is no token).
+    // The wave's maxima per head go to red[v].
+    auto scores = [&](int t, float (&x)[4], float (&sc)[4]) {
+        const uint8_t *T = ring + (t % NS) * G_::kTileBytes;
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
         if constexpr (FP8) {
-            // This wave's rows of tile t landed once at most one later tile of it is in flight.
-            if (live) {
-                if (t + 2 < n_tiles) wait_vm<kLoadsPerWave>();
-                else wait_vm<0>();
-            }
-            Wt = work0;
-            lds_barrier();  // A0: the team's previous tile is fully consumed
-            if (live) {
-                const uint8_t *R = stage_of(t);
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const u32x4 raw = lds_load<u32x4>(R, cv_raw ^ (uint32_t)(cv_flip) ^ (uint32_t)(128 * k));
-                    const u32x2 a0 = e4m3x4_to_bf16x4(raw.x), a1 = e4m3x4_to_bf16x4(raw.y);
-                    const u32x2 a2 = e4m3x4_to_bf16x4(raw.z), a3 = e4m3x4_to_bf16x4(raw.w);
-                    *reinterpret_cast<u32x4 *>(Wt + cv_w0 + 256 * k) = u32x4{a0.x, a0.y, a1.x, a1.y};
-                    *reinterpret_cast<u32x4 *>(Wt + cv_w1 + 256 * k) = u32x4{a2.x, a2.y, a3.x, a3.y};
-                }
-                if (t + 4 < n_tiles) issue(t + 4);  // refills the raw stage just converted
+            for (int jj = 0; jj < 8; ++jj) {
+                const u32x4 raw = lds_load<u32x4>(T, qk_off[jj & 3] + 256 * (jj >> 2));
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e4m3x8_to_bf16x8(raw.x, raw.y)),
+                                                              as_bf16x8(qf[2 * jj]), sa, 0, 0, 0);
+                sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e4m3x8_to_bf16x8(raw.z, raw.w)),
+                                                              as_bf16x8(qf[2 * jj + 1]), sb, 0, 0, 0);
             }
         } else {
-            if (live) wait_vm<0>();
-            Wt = ring + (2 * tm + ((t >> 1) & 1)) * kWorkTile;
-        }
-        lds_barrier();  // A: working tiles complete; tile t-2 of the team fully consumed
-        if constexpr (!FP8) {
-            // bf16 rows land directly in working tiles read by the whole team, so the stage
-            // of tile t-2 is refilled only after barrier A.
-            if (live && t + 2 < n_tiles) issue(t + 2);
-        }
-
-        // ---- logits S^T[token][head] for this wave's 16 tokens x 16 heads (two chains)
-        float x[4], sc[4];
-        float tmax = -INFINITY;
-        if (live) {
-            f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < 16; st += 2) {
-                const u32x4 a0 = lds_load<u32x4>(Wt, qk_off[st & 3] + 256 * (st >> 2));
-                const u32x4 a1 = lds_load<u32x4>(Wt, qk_off[(st + 1) & 3] + 256 * ((st + 1) >> 2));
+                const u32x4 a0 = lds_load<u32x4>(T, qk_off[st & 3] + 256 * (st >> 2));
+                const u32x4 a1 = lds_load<u32x4>(T, qk_off[(st + 1) & 3] + 256 * ((st + 1) >> 2));
                 sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(qf[st]), sa, 0, 0, 0);
                 sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(qf[st + 1]), sb, 0, 0, 0);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int slot = t * kTile + tb + (lane >> 4) * 4 + i;
-                const bool ok = slot < n_slots && rows_s[slot] >= 0;
-                sc[i] = ok ? scale_s[slot] : 0.0f;
-                x[i] = ok ? (sa[i] + sb[i]) * (sm_scale * sc[i]) : -INFINITY;
-                tmax = fmaxf(tmax, x[i]);
-            }
-            tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-            tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-            if (lane < 16) red[wave][lane] = tmax;
         }
-        lds_barrier();  // B: tile maxima
-
-        uint16_t *P = pl[tm];
-        if (live) {
-            const float m_tile = fmaxf(red[wave][lane & 15], red[wave ^ 2][lane & 15]);
-            float alpha = 1.0f;
-            if (m_tile > m_ref + kRescaleSlack) {  // also true for the first tile with a token
-                alpha = m_ref == -INFINITY ? 0.0f : fast_exp(m_ref - m_tile);
-                m_ref = m_tile;
-            }
-            float p[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p[i] = x[i] == -INFINITY ? 0.0f : fast_exp(x[i] - m_ref);
-            l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-            *reinterpret_cast<u32x2 *>(P + qk_head_local * kPStride + tb + (lane >> 4) * 4) =
-                u32x2{pack_bf16x2(p[0] * sc[0], p[1] * sc[1]), pack_bf16x2(p[2] * sc[2], p[3] * sc[3])};
-            if ((v >> 1) == 0 && lane < 16) {
-                alpha_s[tm][qk_head_local] = alpha;
-                if (alpha != 1.0f) rescale_s[tm][par] = 1;
-            }
+        const int s4 = t * kTile + tb + lg * 4;  // four consecutive slots, 16-byte aligned
+        const int4 rw = *reinterpret_cast<const int4 *>(rows_s + s4);
+        f32x4 sv = {1.0f, 1.0f, 1.0f, 1.0f};
+        if constexpr (FP8) {  // rows tb + 4lg .. +3 were fetched by wave (tb + 4lg) >> 3
+            const int rr = tb + lg * 4;
+            sv = *reinterpret_cast<const f32x4 *>(&sc_ring[t % NS][rr >> 3][rr & 7]);
         }
-        if (v == 0 && lane == 0) rescale_s[tm][par ^ 1] = 0;  // read only after the next barrier C
-        lds_barrier();  // C: P, alpha and the rescale flag visible
-
-        // ---- O[head][channel] += P . V over the tile's 32 tokens; this wave: 128 channels.
-        // V fragments come from the working tile with the LDS transpose read: in each 16-lane
-        // group the result lane holds one channel down 4 consecutive tokens; two reads give 8.
-        if (live) {
-            if (rescale_s[tm][par]) {
-                float al[16];
+        const int rwa[4] = {rw.x, rw.y, rw.z, rw.w};
+        float tmax = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) al[i] = alpha_s[tm][8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)];
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = rwa[i] >= 0;
+            sc[i] = ok ? sv[i] : 0.0f;
+            x[i] = ok ? (sa[i] + sb[i]) * (sm_scale * sc[i]) : -INFINITY;
+            tmax = fmaxf(tmax, x[i]);
+        }
+        tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
+        tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+        if (lane < 16) red[v][lane] = tmax;
+    };
+    // After the maxima are exchanged: move the reference maximum if needed, write P (bf16,
+    // fp8 scale folded in) and the rescale factors of tile t (flag parity t&1).
+    auto softmax = [&](int t, const float (&x)[4], const float (&sc)[4]) {
+        const int par = t & 1;
+        const float m_tile = fmaxf(red[v][lane & 15], red[v ^ 2][lane & 15]);
+        float alpha = 1.0f;
+        if (m_tile > m_ref + kRescaleSlack) {  // also true for the first tile with a token
+            alpha = m_ref == -INFINITY ? 0.0f : fast_exp(m_ref - m_tile);
+            m_ref = m_tile;
+        }
+        float p[4];
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
+        for (int i = 0; i < 4; ++i) p[i] = x[i] == -INFINITY ? 0.0f : fast_exp(x[i] - m_ref);
+        l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+        *reinterpret_cast<u32x2 *>(pl + qk_head_local * kPStride + tb + lg * 4) =
+            u32x2{pack_bf16x2(p[0] * sc[0], p[1] * sc[1]), pack_bf16x2(p[2] * sc[2], p[3] * sc[3])};
+        if (v < 2 && lane < 16) {
+            alpha_s[qk_head_local] = alpha;
+            if (alpha != 1.0f) rescale_s[par] = 1;
+        }
+        // The other parity's flag was last read by the products of tile t-1, which every wave
+        // finished before the barrier this phase follows; it is set again for tile t+1.
+        if (v == 0 && lane == 0) rescale_s[par ^ 1] = 0;
+    };
+    // O[head][channel] += P . V over tile t's 32 tokens; this wave: 128 channels. V fragments
+    // come down the token axis through the LDS transpose reads.
+    auto products = [&](int t) {
+        const uint8_t *T = ring + (t % NS) * G_::kTileBytes;
+        if (rescale_s[t & 1]) {
+            float al[16];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[nt][i] *= al[i];
-            }
+            for (int i = 0; i < 16; ++i) al[i] = alpha_s[8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(P + (lane & 31) * kPStride + 16 * ks +
-                                                                 (lane >> 5) * 8);
+            for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
+                for (int i = 0; i < 16; ++i) acc[nt][i] *= al[i];
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(pl + (lane & 31) * kPStride + 16 * ks +
+                                                             (lane >> 5) * 8);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                u32x4 vv;
+                if constexpr (FP8) {
+                    const u32x2 raw = lds_read_tr8(T + v_off[ks][nt]);
+                    vv = e4m3x8_to_bf16x8(raw.x, raw.y);
+                } else {
                     const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t *>(
-                        Wt + v_off[0][nt] + 16 * kWorkRow * ks));
+                        T + v_off[0][nt] + 16 * RB * ks));
                     const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t *>(
-                        Wt + v_off[1][nt] + 16 * kWorkRow * ks));
-                    const u32x4 vv = {lo.x, lo.y, hi.x, hi.y};
-                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(vv),
-                                                                      acc[nt], 0, 0, 0);
+                        T + v_off[1][nt] + 16 * RB * ks));
+                    vv = u32x4{lo.x, lo.y, hi.x, hi.y};
                 }
+                acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(vv),
+                                                                  acc[nt], 0, 0, 0);
             }
         }
-        // The next pair's first barrier orders these reads before the tiles are reused.
+    };
+
+    if constexpr (FP8) {
+        // Software-pipelined: the products of tile t-1 and the scores of tile t are independent
+        // and interleave in one instruction stream. Iteration t first refills the stage of tile
+        // t-2 (its products ended before barrier B of tile t-1) with tile t+2. Per tile two
+        // barriers: B (maxima exchanged; every wave past the products of t-1) and C (P of tile
+        // t visible, tile t+1 resident). P, alpha and the flags of tile t are read by the
+        // products of tile t in the next iteration, before barrier B rewrites them.
+        auto finish_tile = [&](int t, const float (&x)[4], const float (&sc)[4]) {  // t >= 1
+            lds_barrier();  // B
+            softmax(t, x, sc);
+            if (t + 2 < n_tiles) wait_vm<G_::kLoadsT>();  // tile t+1 landed, t+2 may fly
+            else wait_vm<0>();
+            lds_barrier();  // C
+        };
+        if (n_tiles > 0) {
+            float x[4], sc[4];
+            scores(0, x, sc);
+            lds_barrier();  // B; every wave holds its query fragment, so stage 2 is free
+            if (2 < n_tiles) issue(2);
+            softmax(0, x, sc);
+            if (2 < n_tiles) wait_vm<G_::kLoadsT>();
+            else wait_vm<0>();
+            lds_barrier();  // C
+        }
+        for (int t = 1; t < n_tiles; ++t) {
+            float x[4], sc[4];
+            if (t + 2 < n_tiles) issue(t + 2);
+            products(t - 1);
+            scores(t, x, sc);
+            finish_tile(t, x, sc);
+        }
+        if (n_tiles > 0) products(n_tiles - 1);
+    } else {
+        // bf16: one tile in flight (two 32 KiB stages); barrier A opens each tile once it is
+        // resident and the stage of tile t-1 is free for tile t+1 (for t = 0: the query rows
+        // in stage 1 have been read by every wave).
+        for (int t = 0; t < n_tiles; ++t) {
+            float x[4], sc[4];
+            wait_vm<0>();
+            lds_barrier();  // A
+            if (t + 1 < n_tiles) issue(t + 1);
+            scores(t, x, sc);
+            lds_barrier();  // B
+            softmax(t, x, sc);
+            lds_barrier();  // C
+            products(t);
+        }
     }
 
-    // ---- finish: per-head sums of each team, then the two teams are merged
+    wait_vm<0>();  // a tile fetched ahead but past the last token still lands in LDS first
+    // ---- finish: per-head sums (two waves score each head), then out or the split partial
     l_run += shfl_xor_f(l_run, 16);
     l_run += shfl_xor_f(l_run, 32);
     __syncthreads();
-    if (lane < 16) red[wave][lane] = l_run;
+    if (lane < 16) red[v][lane] = l_run;
     __syncthreads();
     if (v < 2 && lane < 16) {
-        lsum_s[tm][qk_head_local] = red[wave][lane] + red[wave ^ 2][lane];
-        msum_s[tm][qk_head_local] = m_ref;
+        lsum_s[qk_head_local] = red[v][lane] + red[v + 2][lane];
+        msum_s[qk_head_local] = m_ref;
     }
     __syncthreads();
-    // Team weights per accumulator row (head) m: exp(m_team - M), M the larger maximum.
-    float wt[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int m = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        const float m0 = msum_s[0][m], m1 = msum_s[1][m];
-        const float M = fmaxf(m0, m1);
-        const float mine = tm == 0 ? m0 : m1;
-        wt[i] = mine == -INFINITY ? 0.0f : fast_exp(mine - M);
-    }
-    float *xch = reinterpret_cast<float *>(ring);  // team 1's weighted O, [32 heads][512]
-    if (tm == 1) {
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const int ch = 128 * v + 32 * nt + (lane & 31);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                xch[m * kC + ch] = acc[nt][i] * wt[i];
-            }
-        }
-    }
-    __syncthreads();
-    if (tm == 1) return;
-
-    float Ls[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int m = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        const float m0 = msum_s[0][m], m1 = msum_s[1][m];
-        const float M = fmaxf(m0, m1);
-        const float w0 = m0 == -INFINITY ? 0.0f : fast_exp(m0 - M);
-        const float w1 = m1 == -INFINITY ? 0.0f : fast_exp(m1 - M);
-        Ls[i] = lsum_s[0][m] * w0 + lsum_s[1][m] * w1;
-    }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int ch = 128 * v + 32 * nt + (lane & 31);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int m = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            acc[nt][i] = acc[nt][i] * wt[i] + xch[m * kC + ch];
-        }
-    }
 
     if (splits == 1) {
 #pragma unroll
@@ -429,84 +474,134 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             for (int i = 0; i < 16; ++i) {
                 const int m = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
                 const int hg = g * 32 + m;
-                if (hg < H) out[((size_t)r * H + hg) * kC + ch] = Ls[i] > 0.0f ? acc[nt][i] / Ls[i] : 0.0f;
+                const float L = lsum_s[m];
+                if (hg < H) out[((size_t)r * H + hg) * kC + ch] = L > 0.0f ? acc[nt][i] / L : 0.0f;
             }
         }
         if (lse != nullptr && tid < 32 && g * 32 + tid < H) {
-            const float M = fmaxf(msum_s[0][tid], msum_s[1][tid]);
-            const float w0 = msum_s[0][tid] == -INFINITY ? 0.0f : fast_exp(msum_s[0][tid] - M);
-            const float w1 = msum_s[1][tid] == -INFINITY ? 0.0f : fast_exp(msum_s[1][tid] - M);
-            const float L = lsum_s[0][tid] * w0 + lsum_s[1][tid] * w1;
-            lse[(size_t)r * H + g * 32 + tid] = L > 0.0f ? M + logf(L) : -INFINITY;
+            const float L = lsum_s[tid];
+            lse[(size_t)r * H + g * 32 + tid] = L > 0.0f ? msum_s[tid] + logf(L) : -INFINITY;
         }
     } else {
-        float *part = ws + (((size_t)r * G + g) * splits + split) * kPartFloats;
+        uint8_t *part = reinterpret_cast<uint8_t *>(ws) + (((size_t)r * G + g) * splits + split) * kPartBytes;
         if (tid < 32) {
-            const float M = fmaxf(msum_s[0][tid], msum_s[1][tid]);
-            const float w0 = msum_s[0][tid] == -INFINITY ? 0.0f : fast_exp(msum_s[0][tid] - M);
-            const float w1 = msum_s[1][tid] == -INFINITY ? 0.0f : fast_exp(msum_s[1][tid] - M);
-            part[tid] = M;
-            part[32 + tid] = lsum_s[0][tid] * w0 + lsum_s[1][tid] * w1;
+            reinterpret_cast<float *>(part)[tid] = msum_s[tid];
+            reinterpret_cast<float *>(part)[32 + tid] = lsum_s[tid];
         }
         if (n_tiles > 0) {  // a split without tokens leaves O unwritten; its sum is 0
+            u32x4 *po = reinterpret_cast<u32x4 *>(part + kPartHeader);
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const int ch = 128 * v + 32 * nt + (lane & 31);
+            for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int m = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                    part[64 + m * kC + ch] = acc[nt][i];
+                for (int i8 = 0; i8 < 2; ++i8) {
+                    const f32x16 &a = acc[nt];
+                    po[((v * 4 + nt) * 2 + i8) * kWave + lane] =
+                        u32x4{pack_bf16x2(a[8 * i8], a[8 * i8 + 1]), pack_bf16x2(a[8 * i8 + 2], a[8 * i8 + 3]),
+                              pack_bf16x2(a[8 * i8 + 4], a[8 * i8 + 5]), pack_bf16x2(a[8 * i8 + 6], a[8 * i8 + 7])};
                 }
-            }
         }
     }
 }
 
-// Merge the per-split partial results of one (row, head): log-sum-exp weights. One block
-// of 128 threads per (row, head); each thread owns 4 channels.
+// Merge the split partials of one (row, head group): block z = 4v + nt covers channels
+// 128v + 32nt .. +31 of all 32 heads. Per head the splits' (max m_s, sum l_s) give
+// M = max m_s, L = sum l_s e^(m_s - M) and the weights e^(m_s - M) / L; out = sum_s weight_s O_s,
+// lse = M + log L. Splits without tokens (l_s = 0) take no part; their O, never written, is
+// read but not used.
 __global__ __launch_bounds__(128) void mla_combine_kernel(int H, int splits,
-                                                          const float *__restrict__ ws,
+                                                          const uint8_t *__restrict__ ws,
                                                           float *__restrict__ out,
                                                           float *__restrict__ lse) {
-    __shared__ float wgt[kMaxSplits];
-    __shared__ float norm_s[2];
+    __shared__ __attribute__((aligned(16))) float wgt[kMaxSplits][32];
+    __shared__ float red4[4][32];
     const int r = blockIdx.x;
-    const int h = blockIdx.y;
-    const int G = (H + 31) / 32;
-    const int g = h >> 5, m = h & 31;
+    const int g = blockIdx.y;
+    const int G = gridDim.y;
+    const int z = blockIdx.z;  // 4v + nt
     const int tid = threadIdx.x;
-    const float *base = ws + ((size_t)r * G + g) * splits * kPartFloats;
-    if (tid < kWave) {
-        // splits <= 64: one lane per split
-        const float ms = tid < splits ? base[(size_t)tid * kPartFloats + m] : -INFINITY;
-        const float ls = tid < splits ? base[(size_t)tid * kPartFloats + 32 + m] : 0.0f;
-        float M = ms;
+    const uint8_t *base = ws + ((size_t)r * G + g) * splits * kPartBytes;
+    const int i8 = tid >> 6, lane = tid & 63;
+    const int slot = (z * 2 + i8) * kWave + lane;   // 16-byte vector within O
+    auto o_vec = [&](int s) {
+        return reinterpret_cast<const u32x4 *>(base + (size_t)s * kPartBytes + kPartHeader)[slot];
+    };
+    // The first 16 splits' O vectors are fetched together with the headers: one round trip.
+    constexpr int kPre = 16;
+    u32x4 pre[kPre];
 #pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) M = fmaxf(M, shfl_xor_f(M, d));
-        const float wv = (ls > 0.0f && M != -INFINITY) ? fast_exp(ms - M) : 0.0f;
-        float L = ls * wv;
+    for (int k = 0; k < kPre; ++k)
+        if (k < splits) pre[k] = o_vec(k);
+    // Weights: thread (head h, quarter q) takes splits q, q+4, ...; the four quarters meet in LDS.
+    {
+        const int h = tid & 31, q = tid >> 5;
+        constexpr int kPer = kMaxSplits / 4;
+        float ms[kPer], ls[kPer];
 #pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) L += shfl_xor_f(L, d);
-        if (tid < splits) wgt[tid] = wv;
-        if (tid == 0) {
-            norm_s[0] = L;
-            norm_s[1] = M;
+        for (int j = 0; j < kPer; ++j) {
+            const int sp = q + 4 * j;
+            ms[j] = -INFINITY;
+            ls[j] = 0.0f;
+            if (sp < splits) {
+                const float *hd = reinterpret_cast<const float *>(base + (size_t)sp * kPartBytes);
+                ms[j] = hd[h];
+                ls[j] = hd[32 + h];
+            }
         }
+        float M = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) M = ls[j] > 0.0f ? fmaxf(M, ms[j]) : M;
+        red4[q][h] = M;
+        __syncthreads();
+        M = fmaxf(fmaxf(red4[0][h], red4[1][h]), fmaxf(red4[2][h], red4[3][h]));
+        float L = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            ms[j] = ls[j] > 0.0f ? fast_exp(ms[j] - M) : 0.0f;
+            L += ls[j] * ms[j];
+        }
+        __syncthreads();
+        red4[q][h] = L;
+        __syncthreads();
+        L = (red4[0][h] + red4[1][h]) + (red4[2][h] + red4[3][h]);
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (q + 4 * j < splits) wgt[q + 4 * j][h] = ms[j] * inv;
+        if (lse != nullptr && z == 0 && q == 0 && g * 32 + h < H)
+            lse[(size_t)r * H + g * 32 + h] = L > 0.0f ? M + logf(L) : -INFINITY;
     }
     __syncthreads();
-    const float L = norm_s[0];
-    const int c = tid * 4;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < splits; ++s) {
-        const float wv = wgt[s];
-        if (wv == 0.0f) continue;  // no token in that split: its O was not written
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(base + (size_t)s * kPartFloats + 64 +
-                                                         m * kC + c);
-        o += v * wv;
+    const int m_lo = 16 * i8 + 4 * (lane >> 5);    // heads m_lo..m_lo+3 and m_lo+8..m_lo+11
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto accumulate = [&](int s, const u32x4 &val) {
+        const f32x4 wl = *reinterpret_cast<const f32x4 *>(&wgt[s][m_lo]);
+        const f32x4 wh = *reinterpret_cast<const f32x4 *>(&wgt[s][m_lo + 8]);
+        const float w[8] = {wl[0], wl[1], wl[2], wl[3], wh[0], wh[1], wh[2], wh[3]};
+        const uint32_t u[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float x = (c & 1) ? bf16_hi(u[c >> 1]) : bf16_lo(u[c >> 1]);
+            o[c] += w[c] != 0.0f ? x * w[c] : 0.0f;
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < kPre; ++k)
+        if (k < splits) accumulate(k, pre[k]);
+    for (int s0 = kPre; s0 < splits; s0 += 8) {  // more splits: eight loads in flight per thread
+        u32x4 val[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (s0 + k < splits) val[k] = o_vec(s0 + k);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (s0 + k < splits) accumulate(s0 + k, val[k]);
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    *reinterpret_cast<f32x4 *>(out + ((size_t)r * H + h) * kC + c) = o * inv;
-    if (lse != nullptr && tid == 0) lse[(size_t)r * H + h] = L > 0.0f ? norm_s[1] + logf(L) : -INFINITY;
+    const int ch = 32 * z + (lane & 31);  // 128v + 32nt + (lane & 31)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int h = g * 32 + m_lo + (c & 3) + 8 * (c >> 2);
+        if (h < H) out[((size_t)r * H + h) * kC + ch] = o[c];
+    }
 }
 
 template <bool FP8, bool PAGED>
@@ -522,14 +617,14 @@ hipError_t launch_v(const MlaPlan &plan, int Q, int W, int H, int B, float sm_sc
                        static_cast<float *>(ws));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.splits == 1) return e;
-    hipLaunchKernelGGL(mla_combine_kernel, dim3(Q, H), dim3(128), 0, stream, H, plan.splits,
-                       static_cast<const float *>(ws), out, lse);
+    hipLaunchKernelGGL(mla_combine_kernel, dim3(Q, plan.groups, 16), dim3(128), 0, stream, H, plan.splits,
+                       static_cast<const uint8_t *>(ws), out, lse);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Split the token slots so that about 256 blocks (one 8-wave block per compute unit) run,
+// Split the token slots so that about 512 blocks (two 4-wave blocks per compute unit) run,
 // with at least 64 slots per split, at most kMaxSplit slots per split and at most
 // kMaxSplits splits; a row that already gives enough blocks is not split.
 MlaPlan plan_sparse_mla(int Q, int W, int H) {
@@ -537,7 +632,7 @@ MlaPlan plan_sparse_mla(int Q, int W, int H) {
     p.groups = (H + 31) / 32;
     const long long wr = ((long long)W + kTile - 1) / kTile * kTile;
     const long long work = (long long)W * Q * p.groups;
-    long long per = (work + 255) / 256;
+    long long per = (work + 511) / 512;
     per = ((per + kTile - 1) / kTile) * kTile;
     if (per < 64) per = 64;
     const long long floor_len = ((wr + kMaxSplits - 1) / kMaxSplits + kTile - 1) / kTile * kTile;
@@ -551,7 +646,7 @@ MlaPlan plan_sparse_mla(int Q, int W, int H) {
         p.splits = (int)((W + per - 1) / per);
     }
     p.split_len = (int)per;
-    p.ws_bytes = p.splits > 1 ? (size_t)Q * p.groups * p.splits * kPartFloats * sizeof(float) : 0;
+    p.ws_bytes = p.splits > 1 ? (size_t)Q * p.groups * p.splits * kPartBytes : 0;
     return p;
 }
 

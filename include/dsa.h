@@ -69,6 +69,8 @@ enum {
 /* Kernel limits of this library: indexer heads per call, index_head_dim values, and the
  * MLA heads handled per 32-head group (more heads run as several groups). */
 #define DSA_MAX_INDEX_HEADS 32
+/* Widest token selection (W, token slots per row) dsa_sparse_mla_decode accepts. */
+#define DSA_MAX_MLA_WIDTH 32768
 
 typedef enum { DSA_BF16 = 0, DSA_F32 = 1, DSA_FP8_E4M3 = 2 } dsa_dtype;
 
@@ -185,6 +187,7 @@ int dsa_expand_selection(const dsa_config *cfg, int Q, int Kw, int B, int S, int
  * block_table [B, max_blocks] i32. Token ids at or past S (when S > 0), blocks mapped to a
  * negative entry, and rows outside [0, kv_rows) are skipped like -1.
  * out: [Q, heads, 512] f32; lse: [Q, heads] f32 or NULL.
+ * W above DSA_MAX_MLA_WIDTH or kv_rows above 2^31 - 1 is refused with DSA_ERR_UNSUPPORTED.
  * ws: device workspace of at least dsa_sparse_mla_decode_workspace(cfg, Q, W) bytes
  * (may be NULL when that is 0). */
 size_t dsa_sparse_mla_decode_workspace(const dsa_config *cfg, int Q, int W);
