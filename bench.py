@@ -1,7 +1,8 @@
 """Decode throughput of the pooled-key DSA path on one MI355X.
 
 One step = one pass of the decode chain over a batch: compact_pools -> index_scores ->
-topk_pools -> expand_selection -> sparse_mla_decode (every launch goes through the C ABI).
+top-k with token-id expansion (one fused launch, dsa_topk_expand) -> sparse_mla_decode (every
+launch goes through the C ABI).
 Default workload: 32 decode queries at contexts log-uniform in [4K, 131,072] tokens,
 index_kpool 8, index_topk 4,096, fp8 pooled keys and fp8 paged 512-wide latent with per-row
 scales, 32 indexer heads x 128 and 32 MLA heads.
@@ -35,9 +36,8 @@ MALL_BYTES = 256 << 20         # Infinity Cache
 KERNEL_SOURCES = {
     "index_scores": "index_scores.hip",
     "sparse_mla_decode": "sparse_mla_decode.hip",
-    "topk_pools": "topk_pools.hip",
+    "topk_expand": "topk_pools.hip",
     "compact_pools": "compact_pools.hip",
-    "expand_selection": "expand_selection.hip",
     "kpool_compress": "kpool_compress.hip",
 }
 
@@ -81,8 +81,7 @@ def algorithmic_bytes(di, n_valid, n_tokens):
     return {
         "compact_pools": B * P + B * P * 4 + B * 4,
         "index_scores": valid_pools * (key_row + 4) + Q * Hi * (2 * D + 4) + Q * P * 5,
-        "topk_pools": Q * P * 5 + Q * wl.kw * 4,
-        "expand_selection": Q * wl.kw * 4 + Q * W * 4,
+        "topk_expand": Q * P * 5 + Q * wl.kw * 4 + Q * W * 4,
         "sparse_mla_decode": n_tokens * tok_row + Q * W * 4 + Q * H * 512 * 2 + Q * H * (512 + 1) * 4,
         # the method's own bytes for the whole step (intermediates excluded)
         "step": valid_pools * key_row + B * P + Q * Hi * (2 * D + 4) + n_tokens * tok_row
@@ -169,10 +168,9 @@ def run_gpu(args):
             s.cfg, s.x.q, s.x.w, s.x.row_seq, s.x.row_pos, s.x.keys, s.ids, s.n_valid,
             first_key=wl.first_key, scale=s.scale, key_scales=s.x.key_scales, scores=s.scores,
             cand=s.cand),
-        "topk_pools": lambda s: dsa.topk_pools(s.cfg, s.scores, s.cand, s.sel),
-        "expand_selection": lambda s: dsa.expand_selection(
-            s.cfg, s.sel, s.x.row_seq, s.x.row_pos, s.x.valid, S=wl.S, first_key=wl.first_key,
-            token_ids=s.token_ids),
+        "topk_expand": lambda s: dsa.topk_expand(
+            s.cfg, s.scores, s.cand, s.x.row_seq, s.x.row_pos, s.x.valid, S=wl.S,
+            first_key=wl.first_key, sel=s.sel, token_ids=s.token_ids),
         "sparse_mla_decode": lambda s: s.attend(),
     }
     stage_us = {}
@@ -317,7 +315,7 @@ def main():
     value = wl.Q / (ms * 1e-3)
 
     # Dominant kernel: the stage with the largest share of the step.
-    dom = max(("index_scores", "sparse_mla_decode", "topk_pools"), key=lambda k: res["stage_us"][k])
+    dom = max(("index_scores", "sparse_mla_decode", "topk_expand"), key=lambda k: res["stage_us"][k])
     dom_us = res["stage_us"][dom]
     achieved = alg[dom] / (dom_us * 1e-6) / 1e9
     traffic = measured_traffic(dom, wl.name)

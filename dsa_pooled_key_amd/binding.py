@@ -33,7 +33,7 @@ ERROR_NAMES = {
 EXPORTED = [
     "dsa_last_error", "dsa_version", "dsa_config_validate", "dsa_select_k", "dsa_out_width",
     "dsa_num_pools", "dsa_kpool_compress", "dsa_compact_pools", "dsa_index_scores",
-    "dsa_topk_pools", "dsa_expand_selection", "dsa_sparse_mla_decode_workspace",
+    "dsa_topk_pools", "dsa_expand_selection", "dsa_topk_expand", "dsa_sparse_mla_decode_workspace",
     "dsa_sparse_mla_decode", "dsa_absorb_q", "dsa_absorb_o", "dsa_f32_to_bf16_rne",
 ]
 
@@ -86,6 +86,7 @@ def lib():
                                   _P, _P, _P], _I),
             "dsa_topk_pools": ([_CFG, _I, _I, _P, _P, _P, _P], _I),
             "dsa_expand_selection": ([_CFG, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P], _I),
+            "dsa_topk_expand": ([_CFG, _I, _I, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P], _I),
             "dsa_sparse_mla_decode_workspace": ([_CFG, _I, _I], _SZ),
             "dsa_sparse_mla_decode": ([_CFG, _I, _I, _I, _F, _P, _P, _P, _P, _I, _P, _I64, _I,
                                        _P, _I, _I, _P, _P, _P, _SZ, _P], _I),
@@ -277,6 +278,33 @@ def expand_selection(cfg: Config, sel, row_seq, row_pos, valid, *, S: int, first
                                       _ptr(row_seq), _ptr(row_pos), _ptr(valid), _ptr(token_ids),
                                       _stream(sel)))
     return token_ids
+
+
+def topk_expand(cfg: Config, scores, cand, row_seq, row_pos, valid, *, S: int, first_key: int,
+                sel=None, token_ids=None):
+    """Fused top-k and expansion: the same (sel, token_ids) as topk_pools then
+    expand_selection. scores/cand [Q,P]; valid [B,S] u8 (read for the tail)."""
+    _dev(scores, "scores", (torch.float32,))
+    Q, P = scores.shape
+    _dev(cand, "cand", (torch.uint8,), (Q, P))
+    _dev(row_seq, "row_seq", (torch.int32,), (Q,))
+    _dev(row_pos, "row_pos", (torch.int32,), (Q,))
+    _dev(valid, "valid", (torch.uint8,))
+    B = valid.shape[0]
+    if valid.shape[1] != S:
+        raise ValueError("valid must be [B, S]")
+    kw = select_k(cfg, P)
+    W = out_width(cfg)
+    if sel is None:
+        sel = torch.empty((Q, kw), dtype=torch.int32, device=scores.device)
+    if token_ids is None:
+        token_ids = torch.empty((Q, W), dtype=torch.int32, device=scores.device)
+    _dev(sel, "sel", (torch.int32,), (Q, kw))
+    _dev(token_ids, "token_ids", (torch.int32,), (Q, W))
+    _check(lib().dsa_topk_expand(ctypes.byref(cfg), Q, P, _ptr(scores), _ptr(cand), B, S,
+                                 first_key, _ptr(row_seq), _ptr(row_pos), _ptr(valid), _ptr(sel),
+                                 _ptr(token_ids), _stream(scores)))
+    return sel, token_ids
 
 
 def sparse_mla_workspace(cfg: Config, Q: int, W: int) -> int:

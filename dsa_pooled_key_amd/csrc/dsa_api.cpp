@@ -229,6 +229,31 @@ int dsa_expand_selection(const dsa_config *cfg, int Q, int Kw, int B, int S, int
                       "expand_selection launch");
 }
 
+int dsa_topk_expand(const dsa_config *cfg, int Q, int P, const float *scores, const uint8_t *cand,
+                    int B, int S, int first_key, const int32_t *row_seq, const int32_t *row_pos,
+                    const uint8_t *valid, int32_t *sel, int32_t *token_ids, hipStream_t stream) {
+    clear_error();
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (Q < 0 || P < 0 || B < 0 || S < 0 || first_key < 0) return set_error(DSA_ERR_BAD_SIZE, "negative size");
+    if (P > dsa::kTopkMaxPools)
+        return set_error(DSA_ERR_UNSUPPORTED, "topk_expand: rows of %d pools exceed the %d this kernel keeps",
+                    P, dsa::kTopkMaxPools);
+    if (P > num_pools(S, first_key, cfg->index_kpool))
+        return set_error(DSA_ERR_BAD_SIZE, "topk_expand: %d pools exceed the %lld that S = %d holds", P,
+                    (long long)num_pools(S, first_key, cfg->index_kpool), S);
+    const int Kw = (int)select_k(cfg, P);
+    const int64_t W = out_width(cfg);
+    if (Q == 0) return DSA_OK;
+    const bool tail = cfg->always_select_tail != 0;
+    if (!token_ids || (Kw > 0 && (!scores || !cand || !sel)) || (tail && (!row_seq || !row_pos || !valid)))
+        return set_error(DSA_ERR_NULL_ARG, "topk_expand: a buffer is NULL");
+    return hip_status(dsa::launch_topk_expand(Q, P, Kw, scores, cand, sel, cfg->index_kpool,
+                                              cfg->index_topk, (int)W, tail, B, S, first_key, row_seq,
+                                              row_pos, valid, token_ids, stream),
+                      "topk_expand launch");
+}
+
 size_t dsa_sparse_mla_decode_workspace(const dsa_config *cfg, int Q, int W) {
     clear_error();
     if (check_config(cfg) || Q < 0 || W < 0 || W > DSA_MAX_MLA_WIDTH) return 0;

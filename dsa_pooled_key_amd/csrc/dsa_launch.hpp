@@ -30,6 +30,12 @@ constexpr int kTopkMaxPools = 65536;
 hipError_t launch_topk_pools(int Q, int P, int Kw, const float *scores, const uint8_t *cand,
                              int32_t *sel, hipStream_t stream);
 
+// Top-k and token-id expansion in one kernel (same results as the two calls in sequence).
+hipError_t launch_topk_expand(int Q, int P, int Kw, const float *scores, const uint8_t *cand,
+                              int32_t *sel, int KP, int topk, int W, bool tail, int B, int S,
+                              int first_key, const int32_t *row_seq, const int32_t *row_pos,
+                              const uint8_t *valid, int32_t *token_ids, hipStream_t stream);
+
 hipError_t launch_expand_selection(int Q, int Kw, int KP, int topk, int W, bool tail, int B,
                                    int S, int first_key, int P, const int32_t *sel,
                                    const int32_t *row_seq, const int32_t *row_pos,

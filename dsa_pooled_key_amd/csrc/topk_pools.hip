@@ -7,11 +7,15 @@
 //
 // One 1024-thread block per row. Thread t keeps the order-preserving 32-bit keys of pools
 // [t*KPT, t*KPT + KPT) in registers (key 0 marks a non-candidate; every candidate maps above
-// it). When there are more candidates than Kw, a most-significant-digit radix select (four
-// 8-bit passes, LDS histogram) finds the Kw-th largest key K*. Every key above K* is taken,
-// plus the lowest-index keys equal to K* (an exclusive prefix count of equal keys in pool
-// order), and a block prefix sum of per-thread counts writes the ids in ascending order.
-// Non-candidates never enter a histogram.
+// it). When there are more candidates than Kw, a most-significant-digit radix select finds
+// the Kw-th largest key K*: the candidates' largest and smallest keys fix the bits they all
+// share, and 8-bit LDS-histogram passes resolve the remaining bits from the highest one that
+// differs (so the first histogram is spread over its bins instead of piling into the few
+// that the float exponent leaves). Every key above K* is taken, plus the lowest-index keys
+// equal to K* (an exclusive prefix count of equal keys in pool order), and a block prefix sum
+// of per-thread counts writes the ids in ascending order. Non-candidates never enter a
+// histogram. The fused variant also writes the row's token ids exactly as expand_selection
+// does, so the selection never goes back to memory to be read again.
 #include "dsa_device.hpp"
 #include "dsa_launch.hpp"
 
@@ -19,100 +23,234 @@ namespace dsa {
 namespace {
 
 constexpr int kThreads = 1024;
+constexpr int kBins = 2 * kThreads;  // value bins of the first stage
 
-template <int KPT>
-__global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw,
+// Token-id expansion of a selection (the expand_selection step), fused into the top-k block.
+struct ExpandArgs {
+    int KP, topk, W, tail, B, S, first_key;
+    const int32_t *row_seq;
+    const int32_t *row_pos;
+    const uint8_t *valid;
+    int32_t *token_ids;
+};
+
+constexpr int kMaxMembers = kWave;  // cutoff bins up to this size are ranked by one wave
+constexpr int kStage = 4096;        // selections up to this width are staged in LDS
+
+template <int KPT, bool EXPAND>
+__global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int vec,
                                                               const float *__restrict__ scores,
                                                               const uint8_t *__restrict__ cand,
-                                                              int32_t *__restrict__ sel) {
+                                                              int32_t *__restrict__ sel,
+                                                              ExpandArgs ex) {
     __shared__ int scratch[kThreads / kWave + 1];
+    __shared__ uint32_t red3[3][kThreads / kWave];
     __shared__ uint32_t hist[256];
-    __shared__ uint32_t pick[2];
+    __shared__ uint32_t bins[kBins];
+    __shared__ uint32_t mem[kMaxMembers];
+    __shared__ int n_mem;
+    __shared__ uint32_t pick[3];
+    __shared__ int32_t sel_s[kStage];
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
     const float *srow = scores + (size_t)r * P;
     const uint8_t *crow = cand + (size_t)r * P;
     const int base = tid * KPT;
 
+    // Keys of pools [base, base + KPT): 16-byte loads where the row allows them.
     uint32_t key[KPT];
+    if (KPT >= 4 && vec && base + KPT <= P) {
+#pragma unroll
+        for (int i = 0; i < KPT; i += 4) {
+            const f32x4 sv = *reinterpret_cast<const f32x4 *>(srow + base + i);
+            const uint32_t cv = *reinterpret_cast<const uint32_t *>(crow + base + i);
+#pragma unroll
+            for (int e = 0; e < 4 && i + e < KPT; ++e)
+                key[i + e] = ((cv >> (8 * e)) & 0xffu) ? ordered_key(sv[e]) : 0u;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int p = base + i;
+            key[i] = (p < P && crow[p]) ? ordered_key(srow[p]) : 0u;
+        }
+    }
+    // Candidate count and the largest and smallest candidate key, in one block reduction.
+    uint32_t nc = 0u, kmax = 0u, kmin = 0xffffffffu;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        const int p = base + i;
-        key[i] = (p < P && crow[p]) ? ordered_key(srow[p]) : 0u;
+        nc += key[i] != 0u;
+        kmax = key[i] > kmax ? key[i] : kmax;
+        if (key[i] != 0u) kmin = key[i] < kmin ? key[i] : kmin;
     }
-    int nc = 0;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) nc += key[i] != 0u;
-    const int n_cand = block_sum<kThreads>(nc, scratch);
+    for (int d = 1; d < kWave; d <<= 1) {  // unsigned comparisons throughout
+        nc += (uint32_t)__shfl_xor((int)nc, d, kWave);
+        const uint32_t om = (uint32_t)__shfl_xor((int)kmax, d, kWave);
+        const uint32_t on = (uint32_t)__shfl_xor((int)kmin, d, kWave);
+        kmax = om > kmax ? om : kmax;
+        kmin = on < kmin ? on : kmin;
+    }
+    if (lane == 0) {
+        red3[0][wave] = nc;
+        red3[1][wave] = kmax;
+        red3[2][wave] = kmin;
+    }
+    if (tid == 0) n_mem = 0;
+    __syncthreads();
+    int n_cand = 0;
+    kmax = 0u;
+    kmin = 0xffffffffu;
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) {
+        n_cand += (int)red3[0][w];
+        kmax = red3[1][w] > kmax ? red3[1][w] : kmax;
+        kmin = red3[2][w] < kmin ? red3[2][w] : kmin;
+    }
     const int take = n_cand < Kw ? n_cand : Kw;
 
     uint32_t thr = 0u;  // take every key > thr, plus `need` of the keys == thr
     int need = 0;
+    int eq_all = n_cand > Kw ? -1 : 0;  // keys == thr when known (then no tie scan is needed)
     if (n_cand > Kw) {
-        uint32_t prefix = 0u, pmask = 0u;
-        int k = Kw;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            if (tid < 256) hist[tid] = 0u;
+        // Stage 1: bucket the candidates by value into kBins equal-width bins between the
+        // smallest and largest score (the bin index never decreases as the score grows), and
+        // find the bin b* holding the Kw-th largest; every key in a higher bin is larger than
+        // every key in b*, every key in a lower one smaller. A span that is zero or not
+        // representable puts everything in bin 0.
+        const float smax = ordered_key_value(kmax), smin = ordered_key_value(kmin);
+        float inv = (float)kBins / (smax - smin);
+        if (!(inv < 3.0e38f)) inv = 0.0f;  // also catches NaN
+        auto bin_of = [&](uint32_t key) {
+            const int bn = (int)((ordered_key_value(key) - smin) * inv);
+            return bn < 0 ? 0 : (bn >= kBins ? kBins - 1 : bn);
+        };
+        for (int i = tid; i < kBins; i += kThreads) bins[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+            if (key[i] != 0u) atomicAdd(&bins[bin_of(key[i])], 1u);
+        __syncthreads();
+        {   // thread t holds bins kBins-1-2t and kBins-2-2t (descending), block prefix sum
+            const uint32_t c0 = bins[kBins - 1 - 2 * tid], c1 = bins[kBins - 2 - 2 * tid];
+            int tot;
+            const int above = block_exclusive_scan<kThreads>((int)(c0 + c1), scratch, &tot);
+            if (above < Kw && Kw <= above + (int)(c0 + c1)) {
+                const bool first = Kw <= above + (int)c0;
+                pick[0] = (uint32_t)(first ? kBins - 1 - 2 * tid : kBins - 2 - 2 * tid);
+                pick[1] = (uint32_t)(first ? above : above + (int)c0);
+                pick[2] = first ? c0 : c1;
+            }
             __syncthreads();
+        }
+        const int bstar = (int)pick[0];
+        int k = Kw - (int)pick[1];  // rank of the cutoff inside b*
+        const int members = (int)pick[2];
+        static_assert(KPT <= 64, "membership mask");
+        uint64_t member = 0u;  // keys of this thread that fall in b*
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+            if (key[i] != 0u && bin_of(key[i]) == bstar) member |= 1ull << i;
+        __syncthreads();  // pick is rewritten below
+        if (members <= kMaxMembers) {
+            // Stage 2 (small bin): gather its keys and let one wave rank them exactly.
 #pragma unroll
             for (int i = 0; i < KPT; ++i)
-                if (key[i] != 0u && (key[i] & pmask) == prefix)
-                    atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
+                if ((member >> i) & 1ull) mem[atomicAdd(&n_mem, 1)] = key[i];
             __syncthreads();
             if (tid < kWave) {
-                // lane l covers digits 255-4l .. 252-4l, scanned from the top
-                const int d0 = 255 - 4 * tid;
-                const uint32_t c0 = hist[d0], c1 = hist[d0 - 1], c2 = hist[d0 - 2], c3 = hist[d0 - 3];
-                const uint32_t s = c0 + c1 + c2 + c3;
-                uint32_t inc = s;
-#pragma unroll
-                for (int d = 1; d < kWave; d <<= 1) {
-                    const uint32_t o = __shfl_up(inc, d, kWave);
-                    if (tid >= d) inc += o;
+                const uint32_t m = tid < members ? mem[tid] : 0u;
+                int gt = 0, eq = 0;
+                for (int j = 0; j < members; ++j) {
+                    const uint32_t o = mem[j];
+                    gt += o > m;
+                    eq += o == m;
                 }
-                const uint32_t above = inc - s;
-                const uint32_t kk = (uint32_t)k;
-                if (above < kk && kk <= inc) {
-                    uint32_t a = above;
-                    int digit = d0;
-                    if (kk > a + c0) {
-                        a += c0;
-                        digit = d0 - 1;
-                        if (kk > a + c1) {
-                            a += c1;
-                            digit = d0 - 2;
-                            if (kk > a + c2) {
-                                a += c2;
-                                digit = d0 - 3;
-                            }
-                        }
-                    }
-                    pick[0] = (uint32_t)digit;
-                    pick[1] = a;
+                if (tid < members && gt < k && k <= gt + eq) {  // equal keys write equal values
+                    pick[0] = m;
+                    pick[1] = (uint32_t)(k - gt);
+                    pick[2] = (uint32_t)eq;
                 }
             }
             __syncthreads();
-            prefix |= pick[0] << shift;
-            pmask |= 255u << shift;
-            k -= (int)pick[1];
-            __syncthreads();
+            thr = pick[0];
+            need = (int)pick[1];
+            eq_all = (int)pick[2];
+        } else {
+            // Stage 2 (large bin, e.g. many equal scores): exact most-significant-digit radix
+            // select of the k-th largest key among the members of b* (8-bit LDS histograms).
+            uint32_t prefix = 0u, pmask = 0u;
+            for (int shift = 24; shift >= 0; shift -= 8) {
+                if (tid < 256) hist[tid] = 0u;
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < KPT; ++i)
+                    if (((member >> i) & 1ull) && (key[i] & pmask) == prefix)
+                        atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
+                __syncthreads();
+                if (tid < kWave) {
+                    // lane l covers digits 255-4l .. 252-4l, scanned from the top
+                    const int d0 = 255 - 4 * tid;
+                    const uint32_t c0 = hist[d0], c1 = hist[d0 - 1], c2 = hist[d0 - 2], c3 = hist[d0 - 3];
+                    const uint32_t sm = c0 + c1 + c2 + c3;
+                    uint32_t inc = sm;
+#pragma unroll
+                    for (int d = 1; d < kWave; d <<= 1) {
+                        const uint32_t o = __shfl_up(inc, d, kWave);
+                        if (tid >= d) inc += o;
+                    }
+                    const uint32_t abv = inc - sm;
+                    const uint32_t kk = (uint32_t)k;
+                    if (abv < kk && kk <= inc) {
+                        uint32_t a = abv;
+                        int digit = d0;
+                        if (kk > a + c0) {
+                            a += c0;
+                            digit = d0 - 1;
+                            if (kk > a + c1) {
+                                a += c1;
+                                digit = d0 - 2;
+                                if (kk > a + c2) {
+                                    a += c2;
+                                    digit = d0 - 3;
+                                }
+                            }
+                        }
+                        pick[0] = (uint32_t)digit;
+                        pick[1] = a;
+                    }
+                }
+                __syncthreads();
+                prefix |= pick[0] << shift;
+                pmask |= 255u << shift;
+                k -= (int)pick[1];
+                __syncthreads();
+            }
+            thr = prefix;
+            need = k;
         }
-        thr = prefix;
-        need = k;
     }
 
+    // Output positions in pool order: every key above thr, plus the first `need` keys equal to
+    // it (the tie scan is skipped when all of them are taken).
     int gt = 0, eq = 0;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
         gt += key[i] > thr;
         eq += key[i] == thr && key[i] != 0u;
     }
-    int eq_total;
-    const int eq_before = block_exclusive_scan<kThreads>(eq, scratch, &eq_total);
-    int take_eq = need - eq_before;
-    take_eq = take_eq < 0 ? 0 : (take_eq > eq ? eq : take_eq);
+    int take_eq = eq;
+    if (eq_all != need) {
+        int eq_total;
+        const int eq_before = block_exclusive_scan<kThreads>(eq, scratch, &eq_total);
+        take_eq = need - eq_before;
+        take_eq = take_eq < 0 ? 0 : (take_eq > eq ? eq : take_eq);
+    }
     int total;
     int o = block_exclusive_scan<kThreads>(gt + take_eq, scratch, &total);
+    const bool staged = Kw <= kStage;
     int32_t *orow = sel + (size_t)r * Kw;
     int eq_seen = 0;
 #pragma unroll
@@ -122,32 +260,94 @@ __global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw,
             s = eq_seen < take_eq;
             ++eq_seen;
         }
-        if (s && o < Kw) orow[o++] = base + i;
+        if (s && o < Kw) {
+            if (staged) sel_s[o] = base + i;
+            else orow[o] = base + i;
+            ++o;
+        }
     }
-    for (int i = take + tid; i < Kw; i += kThreads) orow[i] = -1;
+    if (!staged) {
+        for (int i = take + tid; i < Kw; i += kThreads) orow[i] = -1;
+        if constexpr (EXPAND) {
+            __syncthreads();
+            int32_t *trow = ex.token_ids + (size_t)r * ex.W;
+            for (int j = tid; j < take; j += kThreads) {
+                const int p = orow[j];
+                for (int t = 0; t < ex.KP; ++t) trow[j * ex.KP + t] = ex.first_key + p * ex.KP + t;
+            }
+        }
+    } else {
+        __syncthreads();
+        for (int i = tid; i < Kw; i += kThreads) orow[i] = i < take ? sel_s[i] : -1;
+    }
+    if constexpr (EXPAND) {
+        // Token slots (as expand_selection): selected pool j fills slots j*KP .. j*KP+KP-1,
+        // then -1 up to topk, then the tail tokens after the last whole pool up to row_pos,
+        // each only if valid.
+        int32_t *trow = ex.token_ids + (size_t)r * ex.W;
+        const int b = ex.row_seq[r];
+        const long long pos = ex.row_pos[r];
+        const bool tail_ok = ex.tail && b >= 0 && b < ex.B && pos + 1 > ex.first_key;
+        const long long start = ex.first_key + ((pos + 1 - ex.first_key) / ex.KP) * ex.KP;
+        for (int i = (staged ? 0 : take * ex.KP) + tid; i < ex.W; i += kThreads) {
+            int v = -1;
+            const int j = i / ex.KP;
+            if (j < take) {
+                v = ex.first_key + sel_s[j] * ex.KP + (i - j * ex.KP);
+            } else if (i >= ex.topk && tail_ok) {
+                const long long t = start + (i - ex.topk);
+                if (t <= pos && t < ex.S && ex.valid[(size_t)b * ex.S + t]) v = (int)t;
+            }
+            trow[i] = v;
+        }
+    }
 }
 
 template <int KPT>
 hipError_t launch_kpt(int Q, int P, int Kw, const float *scores, const uint8_t *cand,
-                      int32_t *sel, hipStream_t stream) {
-    hipLaunchKernelGGL(topk_pools_kernel<KPT>, dim3(Q), dim3(kThreads), 0, stream, P, Kw, scores,
-                       cand, sel);
+                      int32_t *sel, const ExpandArgs *ex, hipStream_t stream) {
+    // 16-byte score loads need a 16-byte aligned row start; candidate flags are read 4 at a time.
+    const int vec = (P & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0 &&
+                    (reinterpret_cast<uintptr_t>(cand) & 3) == 0;
+    if (ex)
+        hipLaunchKernelGGL((topk_pools_kernel<KPT, true>), dim3(Q), dim3(kThreads), 0, stream, P,
+                           Kw, vec, scores, cand, sel, *ex);
+    else
+        hipLaunchKernelGGL((topk_pools_kernel<KPT, false>), dim3(Q), dim3(kThreads), 0, stream, P,
+                           Kw, vec, scores, cand, sel, ExpandArgs{});
     return hipGetLastError();
+}
+
+hipError_t launch_any(int Q, int P, int Kw, const float *scores, const uint8_t *cand,
+                      int32_t *sel, const ExpandArgs *ex, hipStream_t stream) {
+    if (Q == 0 || Kw == 0) return hipSuccess;
+    if (P <= kThreads * 1) return launch_kpt<1>(Q, P, Kw, scores, cand, sel, ex, stream);
+    if (P <= kThreads * 2) return launch_kpt<2>(Q, P, Kw, scores, cand, sel, ex, stream);
+    if (P <= kThreads * 4) return launch_kpt<4>(Q, P, Kw, scores, cand, sel, ex, stream);
+    if (P <= kThreads * 8) return launch_kpt<8>(Q, P, Kw, scores, cand, sel, ex, stream);
+    if (P <= kThreads * 16) return launch_kpt<16>(Q, P, Kw, scores, cand, sel, ex, stream);
+    if (P <= kThreads * 32) return launch_kpt<32>(Q, P, Kw, scores, cand, sel, ex, stream);
+    if (P <= kThreads * 64) return launch_kpt<64>(Q, P, Kw, scores, cand, sel, ex, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_topk_pools(int Q, int P, int Kw, const float *scores, const uint8_t *cand,
                              int32_t *sel, hipStream_t stream) {
-    if (Q == 0 || Kw == 0) return hipSuccess;
-    if (P <= kThreads * 1) return launch_kpt<1>(Q, P, Kw, scores, cand, sel, stream);
-    if (P <= kThreads * 2) return launch_kpt<2>(Q, P, Kw, scores, cand, sel, stream);
-    if (P <= kThreads * 4) return launch_kpt<4>(Q, P, Kw, scores, cand, sel, stream);
-    if (P <= kThreads * 8) return launch_kpt<8>(Q, P, Kw, scores, cand, sel, stream);
-    if (P <= kThreads * 16) return launch_kpt<16>(Q, P, Kw, scores, cand, sel, stream);
-    if (P <= kThreads * 32) return launch_kpt<32>(Q, P, Kw, scores, cand, sel, stream);
-    if (P <= kThreads * 64) return launch_kpt<64>(Q, P, Kw, scores, cand, sel, stream);
-    return hipErrorInvalidValue;
+    return launch_any(Q, P, Kw, scores, cand, sel, nullptr, stream);
+}
+
+hipError_t launch_topk_expand(int Q, int P, int Kw, const float *scores, const uint8_t *cand,
+                              int32_t *sel, int KP, int topk, int W, bool tail, int B, int S,
+                              int first_key, const int32_t *row_seq, const int32_t *row_pos,
+                              const uint8_t *valid, int32_t *token_ids, hipStream_t stream) {
+    if (Q == 0 || W == 0) return hipSuccess;
+    if (Kw == 0)  // nothing to select: the plain expansion writes the -1 row and the tail
+        return launch_expand_selection(Q, 0, KP, topk, W, tail, B, S, first_key, P, sel, row_seq,
+                                       row_pos, valid, token_ids, stream);
+    const ExpandArgs ex{KP, topk, W, tail ? 1 : 0, B, S, first_key, row_seq, row_pos, valid, token_ids};
+    return launch_any(Q, P, Kw, scores, cand, sel, &ex, stream);
 }
 
 }  // namespace dsa

@@ -60,8 +60,12 @@ class DeviceDecodeInputs:
 class DecodeStep:
     """One decode (or prefill-chunk) pass of the selection chain and the sparse MLA."""
 
-    def __init__(self, wl: Workload, x: DeviceDecodeInputs, scale: float, sm_scale: float):
+    def __init__(self, wl: Workload, x: DeviceDecodeInputs, scale: float, sm_scale: float,
+                 fused: bool = True):
+        """fused: top-k and token-id expansion in one launch (dsa_topk_expand); otherwise the
+        two entry points in sequence. Both give the same sel and token_ids."""
         self.wl, self.x, self.scale, self.sm_scale = wl, x, scale, sm_scale
+        self.fused = fused
         self.cfg = config_for(wl)
         dev = x.q.device
         B, P, Q = wl.B, wl.pools, wl.Q
@@ -84,9 +88,13 @@ class DecodeStep:
         dsa.index_scores(self.cfg, x.q, x.w, x.row_seq, x.row_pos, x.keys, self.ids, self.n_valid,
                          first_key=wl.first_key, scale=self.scale, key_scales=x.key_scales,
                          scores=self.scores, cand=self.cand)
-        dsa.topk_pools(self.cfg, self.scores, self.cand, self.sel)
-        dsa.expand_selection(self.cfg, self.sel, x.row_seq, x.row_pos, x.valid, S=wl.S,
-                             first_key=wl.first_key, token_ids=self.token_ids)
+        if self.fused:
+            dsa.topk_expand(self.cfg, self.scores, self.cand, x.row_seq, x.row_pos, x.valid,
+                            S=wl.S, first_key=wl.first_key, sel=self.sel, token_ids=self.token_ids)
+        else:
+            dsa.topk_pools(self.cfg, self.scores, self.cand, self.sel)
+            dsa.expand_selection(self.cfg, self.sel, x.row_seq, x.row_pos, x.valid, S=wl.S,
+                                 first_key=wl.first_key, token_ids=self.token_ids)
 
     def attend(self):
         x, wl = self.x, self.wl

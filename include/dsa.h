@@ -173,6 +173,16 @@ int dsa_expand_selection(const dsa_config *cfg, int Q, int Kw, int B, int S, int
                          const int32_t *sel, const int32_t *row_seq, const int32_t *row_pos,
                          const uint8_t *valid, int32_t *token_ids, hipStream_t stream);
 
+/* ------------------------------------------------------------------ steps 4 and 5 fused */
+/* mod.rs, "Shape of the pipeline": the selection and its expansion in one launch. Writes the
+ * same sel [Q, Kw] (Kw = dsa_select_k(cfg, P)) as dsa_topk_pools and the same token_ids
+ * [Q, dsa_out_width(cfg)] as dsa_expand_selection given that sel; the selection is not read
+ * back from memory. P must not exceed dsa_num_pools(S, first_key, kpool) (DSA_ERR_BAD_SIZE).
+ * Arguments as in the two calls; scores, cand and sel may be NULL only when Kw = 0. */
+int dsa_topk_expand(const dsa_config *cfg, int Q, int P, const float *scores, const uint8_t *cand,
+                    int B, int S, int first_key, const int32_t *row_seq, const int32_t *row_pos,
+                    const uint8_t *valid, int32_t *sel, int32_t *token_ids, hipStream_t stream);
+
 /* ------------------------------------------------------------------ step 6 */
 /* build.rs, "The transforms" 1 and 3, and mod.rs (NoPE, 512-wide latent, attention restricted
  * to the selected tokens, paged reads through a block table): for row r and head h, over the

@@ -149,6 +149,11 @@ def test_topk_and_expand_bit_exact_on_oracle_scores(name):
     tok = dsa.expand_selection(cfg, _dev(sel_ref), _dev(di.row_seq[rows]),
                                _dev(di.row_pos[rows]), x.valid, S=wl.S, first_key=wl.first_key)
     assert np.array_equal(tok.cpu().numpy(), tok_ref)
+    # the fused launch gives both at once
+    fsel, ftok = dsa.topk_expand(cfg, _dev(rs), _dev(rc), _dev(di.row_seq[rows]),
+                                 _dev(di.row_pos[rows]), x.valid, S=wl.S, first_key=wl.first_key)
+    assert np.array_equal(fsel.cpu().numpy(), sel_ref)
+    assert np.array_equal(ftok.cpu().numpy(), tok_ref)
 
 
 @pytest.mark.parametrize("P,kw,seed", [(1, 1, 0), (100, 7, 1), (1024, 512, 2), (1025, 512, 3),
@@ -170,7 +175,16 @@ def test_topk_ties_signs_and_row_lengths(P, kw, seed):
     cfg = dsa.Config.make(index_heads=32, index_head_dim=128, index_kpool=1, index_topk=kw,
                           heads=32)
     got = dsa.topk_pools(cfg, _dev(scores), _dev(cand)).cpu().numpy()
-    assert np.array_equal(got, oracle.topk_pools(scores, cand, min(kw, P)))
+    ref = oracle.topk_pools(scores, cand, min(kw, P))
+    assert np.array_equal(got, ref)
+    # fused with expansion (kpool 1: token id = pool id, no tail)
+    zeros = _dev(np.zeros(Q, np.int32))
+    fsel, ftok = dsa.topk_expand(cfg, _dev(scores), _dev(cand), zeros, zeros,
+                                 _dev(np.ones((1, P), np.uint8)), S=P, first_key=0)
+    assert np.array_equal(fsel.cpu().numpy(), ref)
+    tok_ref = np.full((Q, kw), -1, np.int32)
+    tok_ref[:, : ref.shape[1]] = ref
+    assert np.array_equal(ftok.cpu().numpy(), tok_ref)
 
 
 # ------------------------------------------------------------------ step 6: sparse MLA
@@ -287,6 +301,17 @@ def test_selection_chain_exact_twin_bit_exact(name):
     _, _, sel, tok = _oracle_select(di, ids, nv, rows)
     assert np.array_equal(step.sel.cpu().numpy()[rows], sel)
     assert np.array_equal(step.token_ids.cpu().numpy()[rows], tok)
+
+
+@pytest.mark.parametrize("name", ["ragged_fp8", "fp8_mixed_b32", "decode_b4_256k"])
+def test_fused_and_separate_selection_agree(name):
+    di, x, _, _ = case(name)
+    a = DecodeStep(di.wl, x, di.scale, di.sm_scale, fused=True)
+    b = DecodeStep(di.wl, x, di.scale, di.sm_scale, fused=False)
+    a.select()
+    b.select()
+    assert np.array_equal(a.sel.cpu().numpy(), b.sel.cpu().numpy())
+    assert np.array_equal(a.token_ids.cpu().numpy(), b.token_ids.cpu().numpy())
 
 
 @pytest.mark.parametrize("name", ALL)
