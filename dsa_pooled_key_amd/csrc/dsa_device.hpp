@@ -44,6 +44,12 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t codes) {
     return r;
 }
 
+// Eight e4m3 codes (two dwords) -> eight bf16 (four dwords), exact.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+    const u32x2 a = e4m3x4_to_bf16x4(lo), b = e4m3x4_to_bf16x4(hi);
+    return u32x4{a.x, a.y, b.x, b.y};
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 typedef short __attribute__((ext_vector_type(4))) i16x4;

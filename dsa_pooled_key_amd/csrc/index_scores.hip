@@ -13,11 +13,12 @@
 // relu and the head weight, and one cross-lane add with the partner lane (lane ^ 32) finishes
 // the column. Only the [Q, P] score row ever reaches memory.
 //
-// Work split: block (c, r) takes compacted entries [c*256, c*256 + 256) of row r's sequence,
-// 4 waves x 2 tiles of 32 pools. The block also owns the pool-id range from just after the
-// previous block's last id up to its own last id (through P for the last active block) and
-// writes -inf / cand 0 over the non-candidate ids in it, so every slot of the score row is
-// written exactly once and no fill pass is needed.
+// Work split: block (r, c) takes compacted entries [c*256, c*256 + 256) of row r's sequence,
+// 4 waves x 2 tiles of 32 pools, in three dependent round trips (row geometry and query; the
+// count and the block's ids; the keys). The block writes -inf / cand 0 over the ids that are
+// not listed between the previous block's last id and its own last id, and over the ids past
+// the end of the list that fall in its stripe [c*256, c*256 + 256); so every slot of the score
+// row is written exactly once and no fill pass is needed.
 //
 // Bytes per candidate pool: D*2 (bf16 key) or D + 4 (fp8 key and scale), plus 4 (id); the
 // score row costs 5 bytes per pool slot.
@@ -40,116 +41,152 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int32_t *__restrict__ n_valid, float *__restrict__ scores, uint8_t *__restrict__ cand) {
     constexpr int kSteps = D / 16;  // MFMA K-steps of 16 channels (8 per lane half)
     constexpr int kHalf = D / 2;
+    constexpr int kQVec = 32 * D / 8;  // 16-byte pieces of the padded query block
     __shared__ __attribute__((aligned(16))) uint16_t q_s[32 * D];
     __shared__ float w_s[32];
+    __shared__ int ids_s[kChunk + 1];  // ids[j0 - 1 .. j0 + kChunk - 1]
 
-    const int r = blockIdx.y;
-    const int c = blockIdx.x;
+    const int r = blockIdx.x;  // rows vary fastest, so every row's first chunks (the ones
+    const int c = blockIdx.y;  // that hold entries) are dispatched before the empty ones
     const int tid = threadIdx.x;
     float *srow = scores + (size_t)r * P;
     uint8_t *crow = cand + (size_t)r * P;
+    const int j0 = c * kChunk;
 
+    // Round trip 1: everything that does not depend on the row's sequence.
     const int b = row_seq[r];
-    const bool row_ok = b >= 0 && b < B;
     const long long pos = row_pos[r];
+    u32x4 qv[(kQVec + kThreads - 1) / kThreads];
+#pragma unroll
+    for (int k = 0; k < (kQVec + kThreads - 1) / kThreads; ++k) {
+        const int e = (tid + k * kThreads) * 8;  // first element of this piece
+        const int h = e / D;
+        qv[k] = u32x4{0u, 0u, 0u, 0u};
+        if (e < 32 * D && h < Hi) qv[k] = *reinterpret_cast<const u32x4 *>(q + ((size_t)r * Hi) * D + e);
+    }
+    const float wv = tid < 32 && tid < Hi ? w[(size_t)r * Hi + tid] : 0.0f;
+    // Round trip 2: the sequence's valid count and this block's slice of its id list.
+    const bool row_ok = b >= 0 && b < B;
     int nv = row_ok ? n_valid[b] : 0;
     nv = nv < 0 ? 0 : (nv > P ? P : nv);
-    const int j0 = c * kChunk;
-    if (c != 0 && j0 >= nv) return;
-    const int j1 = min(j0 + kChunk, nv);
     const int32_t *idrow = ids + (size_t)(row_ok ? b : 0) * P;
-    auto clampP = [P](int v) { return v < 0 ? 0 : (v > P ? P : v); };
-    const int lo = j0 == 0 ? 0 : clampP(idrow[j0 - 1] + 1);
-    const int hi = j1 >= nv ? P : clampP(idrow[j1 - 1] + 1);
-
-    // Non-candidate ids inside the owned range: the gap before each listed id ...
-    for (int j = j0 + tid; j < j1; j += kThreads) {
-        const int prev = j == j0 ? lo : clampP(idrow[j - 1] + 1);
-        const int cur = min(clampP(idrow[j]), hi);
-        for (int p = prev; p < cur; ++p) {
-            srow[p] = -INFINITY;
-            crow[p] = 0;
-        }
+    const int my_id = j0 + tid < P ? idrow[j0 + tid] : -1;
+    const int prev_id = (tid == 0 && j0 > 0) ? idrow[j0 - 1] : -1;
+#pragma unroll
+    for (int k = 0; k < (kQVec + kThreads - 1) / kThreads; ++k) {
+        const int e = (tid + k * kThreads) * 8;
+        if (e < 32 * D) *reinterpret_cast<u32x4 *>(q_s + e) = qv[k];
     }
-    // ... and the gap after the last one.
-    {
-        const int start = j1 > j0 ? clampP(idrow[j1 - 1] + 1) : lo;
-        for (int p = start + tid; p < hi; p += kThreads) {
-            srow[p] = -INFINITY;
-            crow[p] = 0;
-        }
-    }
-    if (j1 <= j0) return;
-
-    // Stage the row's query (heads padded to 32 with zeros) and head weights.
-    for (int e = tid * 8; e < 32 * D; e += kThreads * 8) {
-        const int h = e / D;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (h < Hi) v = *reinterpret_cast<const u32x4 *>(q + ((size_t)r * Hi) * D + e);
-        *reinterpret_cast<u32x4 *>(q_s + e) = v;
-    }
-    if (tid < 32) w_s[tid] = tid < Hi ? w[(size_t)r * Hi + tid] : 0.0f;
+    if (tid < 32) w_s[tid] = wv;
+    ids_s[1 + tid] = my_id;
+    if (tid == 0) ids_s[0] = prev_id;
     __syncthreads();
-
+    const int j1 = min(j0 + kChunk, nv);
+    auto clampP = [P](int v) { return v < 0 ? 0 : (v > P ? P : v); };
+    auto id_at = [&](int j) { return ids_s[j - j0 + 1]; };  // j in [j0 - 1, j0 + kChunk)
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int n = lane & 31;
     const int half = lane >> 5;
 
-    u32x4 qa[kSteps];
+    // Round trip 3: both tiles' pooled-key half rows are requested before any product, and
+    // with them the id that ends the list (the pools after it are written in stripes below).
+    int pt[kTilesPerWave];
+    bool have[kTilesPerWave], active[kTilesPerWave];
+    u32x4 raw[kTilesPerWave][FP8 ? kHalf / 16 : kSteps];
+    float ksc[kTilesPerWave];
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s)
-        qa[s] = *reinterpret_cast<const u32x4 *>(q_s + n * D + half * kHalf + s * 8);
+    for (int t = 0; t < kTilesPerWave; ++t) {
+        const int jt = j0 + (t * (kThreads / kWave) + wave) * 32;
+        active[t] = jt < j1;
+        const int j = jt + n;
+        int p = (active[t] && j < j1) ? id_at(j) : -1;
+        have[t] = p >= 0 && p < P;
+        if (!have[t]) p = 0;  // a real row: no load is predicated; the column is dropped later
+        pt[t] = p;
+        ksc[t] = 1.0f;
+        if (active[t]) {
+            if constexpr (FP8) {
+                const uint8_t *krow =
+                    static_cast<const uint8_t *>(keys) + ((size_t)b * P + p) * D + half * kHalf;
+#pragma unroll
+                for (int ch = 0; ch < kHalf / 16; ++ch) raw[t][ch] = *reinterpret_cast<const u32x4 *>(krow + ch * 16);
+                ksc[t] = key_scales[(size_t)b * P + p];
+            } else {
+                const uint16_t *krow =
+                    static_cast<const uint16_t *>(keys) + ((size_t)b * P + p) * D + half * kHalf;
+#pragma unroll
+                for (int s = 0; s < kSteps; ++s) raw[t][s] = *reinterpret_cast<const u32x4 *>(krow + s * 8);
+            }
+        }
+    }
+    const int tail = nv > 0 ? clampP(idrow[nv - 1] + 1) : 0;  // first pool after the last listed id
+
+    // Every slot of the score row is written once. Non-candidate ids between this block's
+    // listed ids: the gap before each of them (from just after the previous block's last id)
+    // ...
+    if (j1 > j0) {
+        const int lo = j0 == 0 ? 0 : clampP(id_at(j0 - 1) + 1);
+        for (int j = j0 + tid; j < j1; j += kThreads) {
+            const int prev = j == j0 ? lo : clampP(id_at(j - 1) + 1);
+            const int cur = clampP(id_at(j));
+            for (int p = prev; p < cur; ++p) {
+                srow[p] = -INFINITY;
+                crow[p] = 0;
+            }
+        }
+    }
+    // ... and, in stripes of kChunk pool ids (block c takes [c*kChunk, c*kChunk + kChunk)), every
+    // pool after the last listed id (written at the end, once that id has arrived).
+    auto fill_tail = [&]() {
+        const int p = j0 + tid;
+        if (p >= tail && p < P) {
+            srow[p] = -INFINITY;
+            crow[p] = 0;
+        }
+    };
+    if (j1 <= j0) {
+        fill_tail();
+        return;
+    }
+
+    // The query fragment (A operand: head n, channels half*D/2 + 8s ..) is read from LDS at
+    // each step, which leaves registers for both tiles' keys.
+    const uint16_t *qrow = q_s + n * D + half * kHalf;
     float wr[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) wr[i] = w_s[8 * (i >> 2) + 4 * half + (i & 3)];
 
+#pragma unroll
     for (int t = 0; t < kTilesPerWave; ++t) {
-        const int jt = j0 + (t * (kThreads / kWave) + wave) * 32;
-        if (jt >= j1) break;
-        const int j = jt + n;
-        int p = j < j1 ? idrow[j] : -1;
-        const bool have = p >= 0 && p < P;
-        if (!have) p = 0;
-        const bool is_cand = have && (long long)first_key + (long long)(p + 1) * KP - 1 <= pos;
-
-        // Every lane loads a real key row (p is in range), so no load is predicated; a column
-        // that is not a candidate is dropped in the epilogue, and MFMA columns never mix.
-        u32x4 kb[kSteps];
-        if constexpr (FP8) {
-            const uint8_t *krow =
-                static_cast<const uint8_t *>(keys) + ((size_t)b * P + p) * D + half * kHalf;
-#pragma unroll
-            for (int ch = 0; ch < kHalf / 16; ++ch) {
-                const u32x4 raw = *reinterpret_cast<const u32x4 *>(krow + ch * 16);
-                const u32x2 a = e4m3x4_to_bf16x4(raw.x), bb = e4m3x4_to_bf16x4(raw.y);
-                const u32x2 cc = e4m3x4_to_bf16x4(raw.z), d = e4m3x4_to_bf16x4(raw.w);
-                kb[2 * ch] = u32x4{a.x, a.y, bb.x, bb.y};
-                kb[2 * ch + 1] = u32x4{cc.x, cc.y, d.x, d.y};
-            }
-        } else {
-            const uint16_t *krow =
-                static_cast<const uint16_t *>(keys) + ((size_t)b * P + p) * D + half * kHalf;
-#pragma unroll
-            for (int s = 0; s < kSteps; ++s) kb[s] = *reinterpret_cast<const u32x4 *>(krow + s * 8);
-        }
+        if (!active[t]) break;
+        const int p = pt[t];
+        const bool is_cand = have[t] && (long long)first_key + (long long)(p + 1) * KP - 1 <= pos;
         f32x16 acc = {};
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[s]), as_bf16x8(kb[s]), acc,
-                                                          0, 0, 0);
-        float f = scale;
-        if constexpr (FP8) f *= key_scales[(size_t)b * P + p];
+        for (int s = 0; s < kSteps; ++s) {
+            u32x4 kb;
+            if constexpr (FP8) {
+                const u32x4 rw = raw[t][s >> 1];
+                kb = (s & 1) ? e4m3x8_to_bf16x8(rw.z, rw.w) : e4m3x8_to_bf16x8(rw.x, rw.y);
+            } else {
+                kb = raw[t][s];
+            }
+            const u32x4 qa = *reinterpret_cast<const u32x4 *>(qrow + s * 8);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa), as_bf16x8(kb), acc, 0, 0, 0);
+        }
+        const float f = scale * ksc[t];
         float part = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) part += wr[i] * fmaxf(acc[i] * f, 0.0f);
         float tot = part + shfl_xor_f(part, 32);
         if (tot == 0.0f) tot = 0.0f;
-        if (half == 0 && have) {
+        if (half == 0 && have[t]) {
             srow[p] = is_cand ? tot : -INFINITY;
             crow[p] = is_cand ? 1 : 0;
         }
     }
+    fill_tail();
 }
 
 template <int D, bool FP8>
@@ -159,7 +196,7 @@ hipError_t launch_d(int Q, int B, int P, int Hi, int KP, int first_key, float sc
                     const int32_t *ids, const int32_t *n_valid, float *scores, uint8_t *cand,
                     hipStream_t stream) {
     const int chunks = P > 0 ? (P + kChunk - 1) / kChunk : 1;
-    hipLaunchKernelGGL((index_scores_kernel<D, FP8>), dim3(chunks, Q), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((index_scores_kernel<D, FP8>), dim3(Q, chunks), dim3(kThreads), 0, stream,
                        B, P, Hi, KP, first_key, scale, q, w, row_seq, row_pos, keys, key_scales,
                        ids, n_valid, scores, cand);
     return hipGetLastError();

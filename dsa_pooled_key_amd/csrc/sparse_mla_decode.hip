@@ -109,12 +109,6 @@ __device__ __forceinline__ T lds_load(const uint8_t *base, uint32_t off) {
     return *reinterpret_cast<const T *>(base + off);
 }
 
-// Four e4m3 codes -> four bf16 and eight -> eight (exact).
-__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-    const u32x2 a = e4m3x4_to_bf16x4(lo), b = e4m3x4_to_bf16x4(hi);
-    return u32x4{a.x, a.y, b.x, b.y};
-}
-
 // Block = 4 waves. Wave v scores tile rows 16*(v>>1).. x heads 16*(v&1).. and accumulates O
 // for channels 128v..128v+127 of all 32 heads of group g.
 //
