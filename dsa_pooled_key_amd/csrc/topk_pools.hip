@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int
     __shared__ int scratch[kThreads / kWave + 1];
     __shared__ uint32_t red3[3][kThreads / kWave];
     __shared__ uint32_t hist[256];
-    __shared__ uint32_t bins[kBins];
+    __shared__ __attribute__((aligned(16))) uint32_t bins[kBins];
     __shared__ uint32_t mem[kMaxMembers];
     __shared__ int n_mem;
     __shared__ uint32_t pick[3];
@@ -61,7 +61,20 @@ __global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int
 
     // Keys of pools [base, base + KPT): 16-byte loads where the row allows them.
     uint32_t key[KPT];
-    if (KPT >= 4 && vec && base + KPT <= P) {
+    if (KPT >= 16 && vec && base + KPT <= P) {
+#pragma unroll
+        for (int i = 0; i < KPT; i += 16) {
+            const u32x4 cv = *reinterpret_cast<const u32x4 *>(crow + base + i);
+            const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 sv = *reinterpret_cast<const f32x4 *>(srow + base + i + 4 * q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    key[i + 4 * q + e] = ((cw[q] >> (8 * e)) & 0xffu) ? ordered_key(sv[e]) : 0u;
+            }
+        }
+    } else if (KPT >= 4 && vec && base + KPT <= P) {
 #pragma unroll
         for (int i = 0; i < KPT; i += 4) {
             const f32x4 sv = *reinterpret_cast<const f32x4 *>(srow + base + i);
@@ -133,18 +146,40 @@ __global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int
         for (int i = 0; i < KPT; ++i)
             if (key[i] != 0u) atomicAdd(&bins[bin_of(key[i])], 1u);
         __syncthreads();
-        {   // thread t holds bins kBins-1-2t and kBins-2-2t (descending), block prefix sum
-            const uint32_t c0 = bins[kBins - 1 - 2 * tid], c1 = bins[kBins - 2 - 2 * tid];
-            int tot;
-            const int above = block_exclusive_scan<kThreads>((int)(c0 + c1), scratch, &tot);
-            if (above < Kw && Kw <= above + (int)(c0 + c1)) {
-                const bool first = Kw <= above + (int)c0;
-                pick[0] = (uint32_t)(first ? kBins - 1 - 2 * tid : kBins - 2 - 2 * tid);
-                pick[1] = (uint32_t)(first ? above : above + (int)c0);
-                pick[2] = first ? c0 : c1;
+        if (tid < kWave) {
+            // Wave 0 scans the bins from the top: lane l holds bins kBins-1-32l down to
+            // kBins-32-32l, a wave prefix sum finds the lane, the lane walks its 32 bins.
+            constexpr int kPerLane = kBins / kWave;
+            const int top = kBins - 1 - kPerLane * tid;
+            uint32_t cnt[kPerLane];
+#pragma unroll
+            for (int q = 0; q < kPerLane; q += 4) {
+                const u32x4 v4 = *reinterpret_cast<const u32x4 *>(&bins[top - q - 3]);
+                cnt[q] = v4.w;
+                cnt[q + 1] = v4.z;
+                cnt[q + 2] = v4.y;
+                cnt[q + 3] = v4.x;
             }
-            __syncthreads();
+            uint32_t sum = 0u;
+#pragma unroll
+            for (int q = 0; q < kPerLane; ++q) sum += cnt[q];
+            uint32_t inc = sum;
+#pragma unroll
+            for (int d = 1; d < kWave; d <<= 1) {
+                const uint32_t o = __shfl_up(inc, d, kWave);
+                if (tid >= d) inc += o;
+            }
+            uint32_t above = inc - sum;
+            const uint32_t kk = (uint32_t)Kw;
+            if (above < kk && kk <= inc) {
+                int q = 0;
+                while (kk > above + cnt[q]) above += cnt[q++];
+                pick[0] = (uint32_t)(top - q);
+                pick[1] = above;
+                pick[2] = cnt[q];
+            }
         }
+        __syncthreads();
         const int bstar = (int)pick[0];
         int k = Kw - (int)pick[1];  // rank of the cutoff inside b*
         const int members = (int)pick[2];
@@ -163,8 +198,8 @@ __global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int
             if (tid < kWave) {
                 const uint32_t m = tid < members ? mem[tid] : 0u;
                 int gt = 0, eq = 0;
-                for (int j = 0; j < members; ++j) {
-                    const uint32_t o = mem[j];
+                for (int j = 0; j < members; ++j) {  // lane j's key, broadcast from a register
+                    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)m, j);
                     gt += o > m;
                     eq += o == m;
                 }
@@ -306,9 +341,11 @@ __global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int
 template <int KPT>
 hipError_t launch_kpt(int Q, int P, int Kw, const float *scores, const uint8_t *cand,
                       int32_t *sel, const ExpandArgs *ex, hipStream_t stream) {
-    // 16-byte score loads need a 16-byte aligned row start; candidate flags are read 4 at a time.
-    const int vec = (P & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0 &&
-                    (reinterpret_cast<uintptr_t>(cand) & 3) == 0;
+    // 16-byte score loads need a 16-byte aligned row start; candidate flags are read 16 (or 4)
+    // at a time.
+    const int vec = (KPT >= 16 ? (P & 15) == 0 && (reinterpret_cast<uintptr_t>(cand) & 15) == 0
+                                : (P & 3) == 0 && (reinterpret_cast<uintptr_t>(cand) & 3) == 0) &&
+                    (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
     if (ex)
         hipLaunchKernelGGL((topk_pools_kernel<KPT, true>), dim3(Q), dim3(kThreads), 0, stream, P,
                            Kw, vec, scores, cand, sel, *ex);
