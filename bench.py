@@ -1,8 +1,8 @@
 """Decode throughput of the pooled-key DSA path on one MI355X.
 
-One step = one pass of the decode chain over a batch: compact_pools -> index_scores ->
-top-k with token-id expansion (one fused launch, dsa_topk_expand) -> sparse_mla_decode (every
-launch goes through the C ABI).
+One step = one pass of the decode chain over a batch: pool compaction with index scores (one
+fused launch, dsa_compact_index_scores) -> top-k with token-id expansion (one fused launch,
+dsa_topk_expand) -> sparse_mla_decode (every launch goes through the C ABI).
 Default workload: 32 decode queries at contexts log-uniform in [4K, 131,072] tokens,
 index_kpool 8, index_topk 4,096, fp8 pooled keys and fp8 paged 512-wide latent with per-row
 scales, 32 indexer heads x 128 and 32 MLA heads.
@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 MALL_BYTES = 256 << 20         # Infinity Cache
 KERNEL_SOURCES = {
+    "compact_index_scores": "index_scores.hip",
     "index_scores": "index_scores.hip",
     "sparse_mla_decode": "sparse_mla_decode.hip",
     "topk_expand": "topk_pools.hip",
@@ -81,6 +82,8 @@ def algorithmic_bytes(di, n_valid, n_tokens):
     return {
         "compact_pools": B * P + B * P * 4 + B * 4,
         "index_scores": valid_pools * (key_row + 4) + Q * Hi * (2 * D + 4) + Q * P * 5,
+        # flags of each row's sequence, candidate keys, q and w in; scores and cand out
+        "compact_index_scores": Q * P + valid_pools * key_row + Q * Hi * (2 * D + 4) + Q * P * 5,
         "topk_expand": Q * P * 5 + Q * wl.kw * 4 + Q * W * 4,
         "sparse_mla_decode": n_tokens * tok_row + Q * W * 4 + Q * H * 512 * 2 + Q * H * (512 + 1) * 4,
         # the method's own bytes for the whole step (intermediates excluded)
@@ -109,7 +112,7 @@ def run_gpu(args):
     probe = DecodeStep(wl, x0, di.scale, di.sm_scale)
     probe.run()
     torch.cuda.synchronize()
-    n_valid = probe.n_valid.cpu().numpy()
+    n_valid = (di.pool_valid != 0).sum(axis=1)  # compact_pools' count per sequence
     n_tokens = int((probe.token_ids >= 0).sum().item())
     alg = algorithmic_bytes(di, n_valid, n_tokens)
     touched = alg["step"]
@@ -163,9 +166,8 @@ def run_gpu(args):
 
     # Per-stage durations: each stage alone, same replicas, same graph replay.
     stage_fns = {
-        "compact_pools": lambda s: dsa.compact_pools(s.x.pool_valid, s.ids, s.n_valid),
-        "index_scores": lambda s: dsa.index_scores(
-            s.cfg, s.x.q, s.x.w, s.x.row_seq, s.x.row_pos, s.x.keys, s.ids, s.n_valid,
+        "compact_index_scores": lambda s: dsa.compact_index_scores(
+            s.cfg, s.x.q, s.x.w, s.x.row_seq, s.x.row_pos, s.x.keys, s.x.pool_valid,
             first_key=wl.first_key, scale=s.scale, key_scales=s.x.key_scales, scores=s.scores,
             cand=s.cand),
         "topk_expand": lambda s: dsa.topk_expand(
@@ -322,7 +324,8 @@ def main():
     value = wl.Q / (ms * 1e-3)
 
     # Dominant kernel: the stage with the largest share of the step.
-    dom = max(("index_scores", "sparse_mla_decode", "topk_expand"), key=lambda k: res["stage_us"][k])
+    dom = max(("compact_index_scores", "sparse_mla_decode", "topk_expand"),
+              key=lambda k: res["stage_us"][k])
     dom_us = res["stage_us"][dom]
     achieved = alg[dom] / (dom_us * 1e-6) / 1e9
     traffic = measured_traffic(dom, wl.name)

@@ -33,6 +33,7 @@ ERROR_NAMES = {
 EXPORTED = [
     "dsa_last_error", "dsa_version", "dsa_config_validate", "dsa_select_k", "dsa_out_width",
     "dsa_num_pools", "dsa_kpool_compress", "dsa_compact_pools", "dsa_index_scores",
+    "dsa_compact_index_scores",
     "dsa_topk_pools", "dsa_expand_selection", "dsa_topk_expand", "dsa_sparse_mla_decode_workspace",
     "dsa_sparse_mla_decode", "dsa_absorb_q", "dsa_absorb_o", "dsa_f32_to_bf16_rne",
 ]
@@ -84,6 +85,8 @@ def lib():
             "dsa_compact_pools": ([_I, _I, _P, _P, _P, _P], _I),
             "dsa_index_scores": ([_CFG, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P, _P, _P,
                                   _P, _P, _P], _I),
+            "dsa_compact_index_scores": ([_CFG, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P,
+                                          _P, _P, _P, _P], _I),
             "dsa_topk_pools": ([_CFG, _I, _I, _P, _P, _P, _P], _I),
             "dsa_expand_selection": ([_CFG, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P], _I),
             "dsa_topk_expand": ([_CFG, _I, _I, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P], _I),
@@ -242,6 +245,38 @@ def index_scores(cfg: Config, q, w, row_seq, row_pos, keys, ids, n_valid, *, fir
                                   _ptr(w), _ptr(row_seq), _ptr(row_pos), _ptr(keys), code,
                                   _ptr(key_scales) if code == DSA_FP8_E4M3 else None, _ptr(ids),
                                   _ptr(n_valid), _ptr(scores), _ptr(cand), _stream(q)))
+    return scores, cand
+
+
+def compact_index_scores(cfg: Config, q, w, row_seq, row_pos, keys, pool_valid, *,
+                         first_key: int, scale: float, key_scales=None, scores=None, cand=None):
+    """compact_pools + index_scores in one launch: q [Q,Hi,D] bf16; w [Q,Hi] f32; keys
+    [B,P,D] bf16 or fp8 (+ key_scales [B,P] f32); pool_valid [B,P] u8
+    -> (scores [Q,P] f32, cand [Q,P] u8), equal to index_scores on compact_pools' list."""
+    _dev(q, "q", (torch.bfloat16,))
+    Q, Hi, D = q.shape
+    _dev(w, "w", (torch.float32,), (Q, Hi))
+    _dev(row_seq, "row_seq", (torch.int32,), (Q,))
+    _dev(row_pos, "row_pos", (torch.int32,), (Q,))
+    _dev(keys, "keys", (torch.bfloat16,) + _FP8)
+    B, P, Dk = keys.shape
+    if Dk != D or D != cfg.index_head_dim or Hi != cfg.index_heads:
+        raise ValueError("q / keys shapes differ from the config's indexer geometry")
+    code = _dtype_code(keys)
+    if code == DSA_FP8_E4M3:
+        _dev(key_scales, "key_scales", (torch.float32,), (B, P))
+    _dev(pool_valid, "pool_valid", (torch.uint8,), (B, P))
+    if scores is None:
+        scores = torch.empty((Q, P), dtype=torch.float32, device=q.device)
+    if cand is None:
+        cand = torch.empty((Q, P), dtype=torch.uint8, device=q.device)
+    _dev(scores, "scores", (torch.float32,), (Q, P))
+    _dev(cand, "cand", (torch.uint8,), (Q, P))
+    _check(lib().dsa_compact_index_scores(ctypes.byref(cfg), Q, B, P, first_key, float(scale),
+                                          _ptr(q), _ptr(w), _ptr(row_seq), _ptr(row_pos),
+                                          _ptr(keys), code,
+                                          _ptr(key_scales) if code == DSA_FP8_E4M3 else None,
+                                          _ptr(pool_valid), _ptr(scores), _ptr(cand), _stream(q)))
     return scores, cand
 
 

@@ -191,6 +191,37 @@ int dsa_index_scores(const dsa_config *cfg, int Q, int B, int P, int first_key, 
                       "index_scores launch");
 }
 
+int dsa_compact_index_scores(const dsa_config *cfg, int Q, int B, int P, int first_key,
+                             float scale, const void *q, const float *w, const int32_t *row_seq,
+                             const int32_t *row_pos, const void *keys, dsa_dtype key_dtype,
+                             const float *key_scales, const uint8_t *pool_valid, float *scores,
+                             uint8_t *cand, hipStream_t stream) {
+    clear_error();
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_index_geometry(cfg))) return rc;
+    if (Q < 0 || B < 0 || P < 0 || first_key < 0) return set_error(DSA_ERR_BAD_SIZE, "negative size");
+    if (key_dtype != DSA_BF16 && key_dtype != DSA_FP8_E4M3)
+        return set_error(DSA_ERR_BAD_DTYPE, "compact_index_scores: keys must be bf16 or fp8 e4m3");
+    if (Q == 0 || P == 0) return DSA_OK;
+    if (B == 0) return set_error(DSA_ERR_BAD_SIZE, "compact_index_scores: rows need at least one sequence");
+    if (!q || !w || !row_seq || !row_pos || !keys || !pool_valid || !scores || !cand)
+        return set_error(DSA_ERR_NULL_ARG, "compact_index_scores: a buffer is NULL");
+    const bool fp8 = key_dtype == DSA_FP8_E4M3;
+    if (fp8 && !key_scales)
+        return set_error(DSA_ERR_NULL_ARG, "compact_index_scores: fp8 keys need key_scales");
+    if (!aligned(q, 16) || !aligned(keys, 16))
+        return set_error(DSA_ERR_BAD_SIZE, "compact_index_scores: q and keys need 16-byte alignment");
+    if ((long long)first_key + (long long)P * cfg->index_kpool > 0x7fffffffLL)
+        return set_error(DSA_ERR_BAD_SIZE, "compact_index_scores: token positions exceed int32");
+    return hip_status(dsa::launch_index_scores_valid(Q, B, P, cfg->index_heads, cfg->index_head_dim,
+                                                     cfg->index_kpool, first_key, scale,
+                                                     static_cast<const uint16_t *>(q), w, row_seq,
+                                                     row_pos, keys, fp8, key_scales, pool_valid,
+                                                     scores, cand, stream),
+                      "compact_index_scores launch");
+}
+
 int dsa_topk_pools(const dsa_config *cfg, int Q, int P, const float *scores, const uint8_t *cand,
                    int32_t *sel, hipStream_t stream) {
     clear_error();

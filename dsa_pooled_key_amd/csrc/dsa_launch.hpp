@@ -24,6 +24,12 @@ hipError_t launch_index_scores(int Q, int B, int P, int Hi, int D, int KP, int f
                                bool key_fp8, const float *key_scales, const int32_t *ids,
                                const int32_t *n_valid, float *scores, uint8_t *cand,
                                hipStream_t stream);
+hipError_t launch_index_scores_valid(int Q, int B, int P, int Hi, int D, int KP, int first_key,
+                                     float scale, const uint16_t *q, const float *w,
+                                     const int32_t *row_seq, const int32_t *row_pos,
+                                     const void *keys, bool key_fp8, const float *key_scales,
+                                     const uint8_t *pool_valid, float *scores, uint8_t *cand,
+                                     hipStream_t stream);
 
 // Largest row length the top-k kernel keeps in registers.
 constexpr int kTopkMaxPools = 65536;

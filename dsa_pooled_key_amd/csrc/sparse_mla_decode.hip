@@ -172,11 +172,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // without a token fetches latent row 0 (finite data; its weight is zero).
     const int dma_rl = lane / G_::kLanesPerRow;                    // row within one load
     const uint32_t dma_col = 16 * ((lane % G_::kLanesPerRow));     // byte position in the row
-    auto issue = [&](int t) {
+    // The wave's 8 latent rows of tile t (and, for fp8, lane&7's row for the scale copy) are
+    // read from rows_s first; issue_rows() then starts the copies.
+    struct TileRows {
+        int4 a, b;
+        int srow;
+    };
+    auto read_rows = [&](int t) {
+        TileRows tr;
+        tr.a = *reinterpret_cast<const int4 *>(rows_s + t * kTile + 8 * v);
+        tr.b = *reinterpret_cast<const int4 *>(rows_s + t * kTile + 8 * v + 4);
+        tr.srow = FP8 ? rows_s[t * kTile + 8 * v + (lane & 7)] : 0;
+        return tr;
+    };
+    auto issue_rows = [&](int t, const TileRows &tr) {
         uint8_t *stage = ring + (t % NS) * G_::kTileBytes + 8 * v * RB;
-        const int4 ra = *reinterpret_cast<const int4 *>(rows_s + t * kTile + 8 * v);
-        const int4 rb = *reinterpret_cast<const int4 *>(rows_s + t * kTile + 8 * v + 4);
-        const int rws[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+        const int rws[8] = {tr.a.x, tr.a.y, tr.a.z, tr.a.w, tr.b.x, tr.b.y, tr.b.z, tr.b.w};
 #pragma unroll
         for (int k = 0; k < G_::kLoads; ++k) {
             const int rl = k * G_::kRowsPerLoad;  // first row of this load within the wave's 8
@@ -186,11 +197,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             const uint8_t *src = kvb + (size_t)prow * RB + (dma_col ^ (uint32_t)(16 * swz<FP8>(rr)));
             dma16(src, __builtin_amdgcn_readfirstlane(lds_offset(stage + k * 1024)));
         }
-        if constexpr (FP8) {
-            const int srow = max(rows_s[t * kTile + 8 * v + (lane & 7)], 0);
-            dma4(kv_scales + srow, __builtin_amdgcn_readfirstlane(lds_offset(&sc_ring[t % NS][v][0])));
-        }
+        if constexpr (FP8)
+            dma4(kv_scales + max(tr.srow, 0),
+                 __builtin_amdgcn_readfirstlane(lds_offset(&sc_ring[t % NS][v][0])));
     };
+    auto issue = [&](int t) { issue_rows(t, read_rows(t)); };
 
     // ---- prologue: wave v resolves the slots its own DMA fetches -- slot t*32 + 8v + j of
     // every tile t -- to latent rows (or -1) and issues the first tiles at once; it reads
@@ -297,6 +308,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // Scores S^T[token][head] for this wave's 16 tokens x 16 heads (two MFMA chains), scaled
     // and masked into x; sc gets the rows' fp8 scales (1 for bf16, 0 where there is no token).
     // The wave's maxima per head go to red[v].
+    // Slots tb + 4lg .. +3 of tile t (16-byte aligned) and, for fp8, their rows' scales (rows
+    // tb + 4lg .. +3 were fetched by wave (tb + 4lg) >> 3).
+    auto score_rows = [&](int t) {
+        return *reinterpret_cast<const int4 *>(rows_s + t * kTile + tb + lg * 4);
+    };
+    auto score_scales = [&](int t) {
+        f32x4 sv = {1.0f, 1.0f, 1.0f, 1.0f};
+        if constexpr (FP8) {
+            const int rr = tb + lg * 4;
+            sv = *reinterpret_cast<const f32x4 *>(&sc_ring[t % NS][rr >> 3][rr & 7]);
+        }
+        return sv;
+    };
+    auto score_epilogue = [&](const f32x4 &sa, const f32x4 &sb, const int4 &rw, const f32x4 &sv,
+                              float (&x)[4], float (&sc)[4]) {
+        const int rwa[4] = {rw.x, rw.y, rw.z, rw.w};
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = rwa[i] >= 0;
+            sc[i] = ok ? sv[i] : 0.0f;
+            x[i] = ok ? (sa[i] + sb[i]) * (sm_scale * sc[i]) : -INFINITY;
+            tmax = fmaxf(tmax, x[i]);
+        }
+        tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
+        tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+        if (lane < 16) red[v][lane] = tmax;
+    };
     auto scores = [&](int t, float (&x)[4], float (&sc)[4]) {
         const uint8_t *T = ring + (t % NS) * G_::kTileBytes;
         f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
@@ -318,25 +357,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(qf[st + 1]), sb, 0, 0, 0);
             }
         }
-        const int s4 = t * kTile + tb + lg * 4;  // four consecutive slots, 16-byte aligned
-        const int4 rw = *reinterpret_cast<const int4 *>(rows_s + s4);
-        f32x4 sv = {1.0f, 1.0f, 1.0f, 1.0f};
-        if constexpr (FP8) {  // rows tb + 4lg .. +3 were fetched by wave (tb + 4lg) >> 3
-            const int rr = tb + lg * 4;
-            sv = *reinterpret_cast<const f32x4 *>(&sc_ring[t % NS][rr >> 3][rr & 7]);
-        }
-        const int rwa[4] = {rw.x, rw.y, rw.z, rw.w};
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool ok = rwa[i] >= 0;
-            sc[i] = ok ? sv[i] : 0.0f;
-            x[i] = ok ? (sa[i] + sb[i]) * (sm_scale * sc[i]) : -INFINITY;
-            tmax = fmaxf(tmax, x[i]);
-        }
-        tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-        tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-        if (lane < 16) red[v][lane] = tmax;
+        const int4 rw = score_rows(t);
+        const f32x4 sv = score_scales(t);
+        score_epilogue(sa, sb, rw, sv, x, sc);
     };
     // After the maxima are exchanged: move the reference maximum if needed, write P (bf16,
     // fp8 scale folded in) and the rescale factors of tile t (flag parity t&1).
@@ -364,17 +387,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     };
     // O[head][channel] += P . V over tile t's 32 tokens; this wave: 128 channels. V fragments
     // come down the token axis through the LDS transpose reads.
+    auto rescale_acc = [&]() {
+        float al[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) al[i] = alpha_s[8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[nt][i] *= al[i];
+    };
     auto products = [&](int t) {
         const uint8_t *T = ring + (t % NS) * G_::kTileBytes;
-        if (rescale_s[t & 1]) {
-            float al[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) al[i] = alpha_s[8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)];
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[nt][i] *= al[i];
-        }
+        if (rescale_s[t & 1]) rescale_acc();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const u32x4 a = *reinterpret_cast<const u32x4 *>(pl + (lane & 31) * kPStride + 16 * ks +
@@ -422,11 +446,58 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             else wait_vm<0>();
             lds_barrier();  // C
         }
+        // Iteration t: every LDS operand of the refill, of the products of tile t-1 and of the
+        // scores of tile t is requested before the first is used, so their latencies overlap
+        // one another and the MFMA work instead of adding up.
+        auto step = [&](int t, float (&x)[4], float (&sc)[4]) {
+            const bool refill = t + 2 < n_tiles;
+            const uint8_t *TP = ring + ((t - 1) % NS) * G_::kTileBytes;
+            const uint8_t *TS = ring + (t % NS) * G_::kTileBytes;
+            TileRows nr{};
+            if (refill) nr = read_rows(t + 2);
+            const int resc = rescale_s[(t - 1) & 1];
+            u32x4 pa[2];
+            u32x2 vr[2][4];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                pa[ks] = *reinterpret_cast<const u32x4 *>(pl + (lane & 31) * kPStride + 16 * ks +
+                                                          (lane >> 5) * 8);
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) vr[ks][nt] = lds_read_tr8(TP + v_off[ks][nt]);
+            }
+            u32x4 kr[8];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) kr[jj] = lds_load<u32x4>(TS, qk_off[jj]);
+            const int4 rw = score_rows(t);
+            const f32x4 sv = score_scales(t);
+            __builtin_amdgcn_sched_barrier(0);
+            if (refill) issue_rows(t + 2, nr);
+            if (resc) rescale_acc();
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        as_bf16x8(pa[ks]), as_bf16x8(e4m3x8_to_bf16x8(vr[ks][nt].x, vr[ks][nt].y)),
+                        acc[nt], 0, 0, 0);
+            // The second half of the key chunks takes the registers the V fragments held.
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int jj = 4; jj < 8; ++jj) kr[jj] = lds_load<u32x4>(TS, qk_off[jj & 3] + 256);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e4m3x8_to_bf16x8(kr[jj].x, kr[jj].y)),
+                                                              as_bf16x8(qf[2 * jj]), sa, 0, 0, 0);
+                sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(e4m3x8_to_bf16x8(kr[jj].z, kr[jj].w)),
+                                                              as_bf16x8(qf[2 * jj + 1]), sb, 0, 0, 0);
+            }
+            score_epilogue(sa, sb, rw, sv, x, sc);
+        };
         for (int t = 1; t < n_tiles; ++t) {
             float x[4], sc[4];
-            if (t + 2 < n_tiles) issue(t + 2);
-            products(t - 1);
-            scores(t, x, sc);
+            step(t, x, sc);
             finish_tile(t, x, sc);
         }
         if (n_tiles > 0) products(n_tiles - 1);

@@ -2,7 +2,8 @@
 
 ``DecodeStep`` owns the intermediate and output buffers of one batch and issues
 compact_pools -> index_scores -> topk_pools -> expand_selection -> sparse_mla_decode on the
-current stream through the C ABI. It allocates only in its constructor, so ``run()`` can be
+current stream through the C ABI (fused: compact_index_scores -> topk_expand ->
+sparse_mla_decode, three launches of the same steps). It allocates only in its constructor, so ``run()`` can be
 recorded into a HIP graph (``torch.cuda.CUDAGraph``) and replayed.
 """
 from __future__ import annotations
@@ -62,8 +63,9 @@ class DecodeStep:
 
     def __init__(self, wl: Workload, x: DeviceDecodeInputs, scale: float, sm_scale: float,
                  fused: bool = True):
-        """fused: top-k and token-id expansion in one launch (dsa_topk_expand); otherwise the
-        two entry points in sequence. Both give the same sel and token_ids."""
+        """fused: compaction and scoring in one launch (dsa_compact_index_scores) and top-k
+        with token-id expansion in one launch (dsa_topk_expand); otherwise the five entry
+        points in sequence. Both give the same scores, cand, sel and token_ids."""
         self.wl, self.x, self.scale, self.sm_scale = wl, x, scale, sm_scale
         self.fused = fused
         self.cfg = config_for(wl)
@@ -84,10 +86,15 @@ class DecodeStep:
 
     def select(self):
         x, wl = self.x, self.wl
-        dsa.compact_pools(x.pool_valid, self.ids, self.n_valid)
-        dsa.index_scores(self.cfg, x.q, x.w, x.row_seq, x.row_pos, x.keys, self.ids, self.n_valid,
-                         first_key=wl.first_key, scale=self.scale, key_scales=x.key_scales,
-                         scores=self.scores, cand=self.cand)
+        if self.fused:
+            dsa.compact_index_scores(self.cfg, x.q, x.w, x.row_seq, x.row_pos, x.keys,
+                                     x.pool_valid, first_key=wl.first_key, scale=self.scale,
+                                     key_scales=x.key_scales, scores=self.scores, cand=self.cand)
+        else:
+            dsa.compact_pools(x.pool_valid, self.ids, self.n_valid)
+            dsa.index_scores(self.cfg, x.q, x.w, x.row_seq, x.row_pos, x.keys, self.ids,
+                             self.n_valid, first_key=wl.first_key, scale=self.scale,
+                             key_scales=x.key_scales, scores=self.scores, cand=self.cand)
         if self.fused:
             dsa.topk_expand(self.cfg, self.scores, self.cand, x.row_seq, x.row_pos, x.valid,
                             S=wl.S, first_key=wl.first_key, sel=self.sel, token_ids=self.token_ids)

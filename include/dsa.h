@@ -9,6 +9,7 @@
  *   k, gate, valid, ape -> dsa_kpool_compress   -> pooled keys, pool validity
  *                       -> dsa_compact_pools    -> ascending valid pool ids per sequence
  *                       -> dsa_index_scores     -> [Q, P] scores + candidate flags
+ *                          (dsa_compact_index_scores: steps 2 and 3 in one launch)
  *                       -> dsa_topk_pools       -> [Q, select_k] pool ids
  *                       -> dsa_expand_selection -> [Q, out_width] token ids (-1 = none)
  *                       -> dsa_sparse_mla_decode -> [Q, heads, 512] latent-space output
@@ -152,6 +153,20 @@ int dsa_index_scores(const dsa_config *cfg, int Q, int B, int P, int first_key, 
                      const int32_t *row_pos, const void *keys, dsa_dtype key_dtype,
                      const float *key_scales, const int32_t *ids, const int32_t *n_valid,
                      float *scores, uint8_t *cand, hipStream_t stream);
+
+/* ------------------------------------------------------------------ steps 2 and 3 fused */
+/* mod.rs, "Shape of the pipeline" (dsa_compact_pools, then dsa_index_scores), in one launch:
+ * pool p is a candidate for row r when pool_valid[b, p] != 0 (b = row_seq[r]) and its last
+ * token first_key + (p+1)*KP - 1 <= row_pos[r]. scores and cand are exactly those of
+ * dsa_compact_pools followed by dsa_index_scores on the same flags; the compacted id list is
+ * never materialised (each block reads the flags of its own pool range and loads keys only for
+ * candidates, which is the read the compaction saves).
+ * pool_valid: [B, P] u8 (dsa_kpool_compress output); the other arguments as dsa_index_scores. */
+int dsa_compact_index_scores(const dsa_config *cfg, int Q, int B, int P, int first_key,
+                             float scale, const void *q, const float *w, const int32_t *row_seq,
+                             const int32_t *row_pos, const void *keys, dsa_dtype key_dtype,
+                             const float *key_scales, const uint8_t *pool_valid, float *scores,
+                             uint8_t *cand, hipStream_t stream);
 
 /* ------------------------------------------------------------------ step 4 */
 /* mod.rs, "Shape of the pipeline": [Q, select_k] pool ids. Per row, the Kw candidates that

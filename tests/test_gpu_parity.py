@@ -131,6 +131,91 @@ def test_index_scores_exact_twin_bit_exact(name):
     assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32))
 
 
+# ------------------------------------------------------------------ steps 2 and 3 in one launch
+
+def _compact_index(di, x, pool_valid=None, row_seq=None, row_pos=None):
+    wl = di.wl
+    return dsa.compact_index_scores(
+        config_for(wl), x.q, x.w, x.row_seq if row_seq is None else row_seq,
+        x.row_pos if row_pos is None else row_pos, x.keys,
+        x.pool_valid if pool_valid is None else pool_valid, first_key=wl.first_key,
+        scale=di.scale, key_scales=x.key_scales)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_compact_index_scores(name):
+    di, x, ids, nv = case(name)
+    scores, cand = _compact_index(di, x)
+    rows = _rows(di, 14)
+    rs, rc = _oracle_scores(di, ids, nv, rows)
+    gs, gc = scores.cpu().numpy()[rows], cand.cpu().numpy()[rows]
+    assert np.array_equal(gc, rc)
+    assert np.all(np.isneginf(gs[rc == 0]))
+    assert not np.any(np.signbit(gs[rc == 1]) & (gs[rc == 1] == 0))
+    _check_scores(gs, rs, rc)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_compact_index_scores_exact_twin_bit_exact(name):
+    di, x, ids, nv = case(name, exact=True)
+    scores, cand = _compact_index(di, x)
+    rows = _rows(di, 6)
+    rs, rc = _oracle_scores(di, ids, nv, rows)
+    gs, gc = scores.cpu().numpy()[rows], cand.cpu().numpy()[rows]
+    assert np.array_equal(gc, rc)
+    assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_fp8", "ragged_prefill", "fp8_mixed_b32",
+                                  "decode_b4_256k"])
+def test_compact_index_scores_equals_the_two_calls(name):
+    """Every slot of every row, bit for bit, against compact_pools + index_scores."""
+    di, x, _, _ = case(name)
+    wl = di.wl
+    cfg = config_for(wl)
+    ids = torch.empty((wl.B, wl.pools), dtype=torch.int32, device=x.q.device)
+    nv = torch.empty((wl.B,), dtype=torch.int32, device=x.q.device)
+    dsa.compact_pools(x.pool_valid, ids, nv)
+    s2, c2 = dsa.index_scores(cfg, x.q, x.w, x.row_seq, x.row_pos, x.keys, ids, nv,
+                              first_key=wl.first_key, scale=di.scale, key_scales=x.key_scales)
+    s1, c1 = _compact_index(di, x)
+    assert np.array_equal(c1.cpu().numpy(), c2.cpu().numpy())
+    assert np.array_equal(s1.cpu().numpy().view(np.uint32), s2.cpu().numpy().view(np.uint32))
+
+
+def test_compact_index_scores_edge_rows():
+    """Rows outside the batch, a position before first_key, a position in the middle of a pool
+    over a sequence whose flags are all nonzero (not only 1), a sequence with no valid pool;
+    374 pools, so the last tile of a row is ragged."""
+    di, x, _, _ = case("ragged_fp8")
+    wl = di.wl
+    Q, B, P = wl.Q, wl.B, wl.pools
+    assert Q == 5 and list(di.row_seq) == [0, 1, 2, 3, 4] and P % 32 != 0
+    row_seq = di.row_seq.copy()
+    row_pos = di.row_pos.copy()
+    row_seq[0] = -1
+    row_seq[1] = B
+    row_pos[2] = wl.first_key - 1
+    row_pos[3] = wl.first_key + 5 * wl.kpool + wl.kpool // 2
+    pv = di.pool_valid.copy()
+    pv[3] = np.random.default_rng(7).integers(1, 3, size=P)
+    pv[4] = 0
+    ids, nv = oracle.compact_pools(pv)
+    scores, cand = _compact_index(di, x, pool_valid=_dev(pv), row_seq=_dev(row_seq),
+                                  row_pos=_dev(row_pos))
+    gs, gc = scores.cpu().numpy(), cand.cpu().numpy()
+    # rows 0 and 1 name no sequence of the batch: every slot is a non-candidate
+    assert not gc[:2].any() and np.all(np.isneginf(gs[:2]))
+    ok = np.arange(2, Q)
+    rs, rc = oracle.index_scores(di.q[ok], di.w[ok], row_seq[ok], row_pos[ok], di.keys, ids, nv,
+                                 kpool=wl.kpool, first_key=wl.first_key, scale=di.scale,
+                                 key_scales=di.key_scales)
+    assert np.array_equal(gc[ok], rc)
+    assert rc[0].sum() == 0 and rc[1].sum() == 5 and rc[2].sum() == 0
+    assert np.all(np.isneginf(gs[ok][rc == 0]))
+    _check_scores(gs[ok], rs, rc)
+
+
 # ------------------------------------------------------------------ steps 4 and 5
 
 @pytest.mark.parametrize("name", ALL)
