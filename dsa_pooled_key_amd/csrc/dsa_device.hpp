@@ -93,38 +93,112 @@ __device__ __forceinline__ float ordered_key_value(uint32_t k) {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// gfx950 lane swaps (v_permlane16_swap / v_permlane32_swap) applied to two copies of v: the
+// pair holds v of rows {0,0,2,2} and {1,1,3,3} (16-lane rows), or of lanes 0-31 and 32-63 each
+// repeated twice, so op(first, second) reduces across lanes l and l ^ 16 (or l ^ 32) in two
+// VALU instructions and no LDS trip.
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float add_xor16(float v) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// ------------------------------------------------------------------ wave primitives (DPP)
+// Cross-lane steps through DPP (the VALU reads a neighbour lane's register in the same
+// instruction), not through LDS: GFX9 controls quad_perm, row_shr:n, row_ror:n (rows are 16
+// lanes) and row_bcast:15/31. All of these are used with the whole wave active.
+namespace dpp {
+constexpr int kXor1 = 0xb1;        // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4e;        // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
+constexpr int kRowShr1 = 0x111;
+constexpr int kRowShr2 = 0x112;
+constexpr int kRowShr4 = 0x114;
+constexpr int kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142;  // lane 15 of each row to the whole next row
+constexpr int kRowBcast31 = 0x143;  // lane 31 to rows 2 and 3
+}  // namespace dpp
+
+// v of the DPP source lane; 0 where the control gives no source or the row is masked off.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xf, 0xf, false);
+}
+
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele in each row, then the row carries).
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+    v += dpp_or_zero<dpp::kRowShr1>(v);
+    v += dpp_or_zero<dpp::kRowShr2>(v);
+    v += dpp_or_zero<dpp::kRowShr4>(v);
+    v += dpp_or_zero<dpp::kRowShr8>(v);
+    v += dpp_or_zero<dpp::kRowBcast15, 0xa>(v);
+    v += dpp_or_zero<dpp::kRowBcast31, 0xc>(v);
+    return v;
+}
+
+// Reductions over the 64 lanes: a butterfly inside each row, then the four row results
+// (lanes 0, 16, 32, 48) read into scalars. The result is wave-uniform.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+    v = op(v, dpp_mov<dpp::kXor1>(v));
+    v = op(v, dpp_mov<dpp::kXor2>(v));
+    v = op(v, dpp_mov<dpp::kRowRor4>(v));
+    v = op(v, dpp_mov<dpp::kRowRor8>(v));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return op(op(a, b), op(c, d));
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+    return wave_reduce_u32(v, [](uint32_t x, uint32_t y) { return x + y; });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    return wave_reduce_u32(v, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    return wave_reduce_u32(v, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+}
+
 // ------------------------------------------------------------------ block scans
 // Exclusive prefix sum over a block of NT threads (NT a multiple of 64, at most 1024).
 // `scratch` must hold NT/64 + 1 ints. Returns the exclusive prefix; *total gets the sum.
+// Each wave scans in registers and publishes its total; after one barrier every thread adds
+// the totals of the waves before its own. A trailing barrier lets the caller reuse scratch.
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int *scratch, int *total) {
+    constexpr int NW = NT / kWave;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    int inc = v;
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        int o = __shfl_up(inc, d, kWave);
-        if (lane >= d) inc += o;
-    }
+    const int inc = (int)wave_incl_sum((uint32_t)v);
     if (lane == kWave - 1) scratch[wave] = inc;
     __syncthreads();
-    if (wave == 0) {
-        constexpr int NW = NT / kWave;
-        int x = lane < NW ? scratch[lane] : 0;
-        int xi = x;
+    int before = 0, all = 0;
 #pragma unroll
-        for (int d = 1; d < NW; d <<= 1) {
-            int o = __shfl_up(xi, d, kWave);
-            if (lane >= d) xi += o;
-        }
-        if (lane < NW) scratch[lane] = xi - x;
-        if (lane == NW - 1) scratch[NW] = xi;
+    for (int w = 0; w < NW; ++w) {
+        const int x = scratch[w];
+        before += w < wave ? x : 0;
+        all += x;
     }
+    *total = all;
     __syncthreads();
-    int excl = scratch[wave] + inc - v;
-    *total = scratch[NT / kWave];
-    __syncthreads();
-    return excl;
+    return before + inc - v;
 }
 
 template <int NT>

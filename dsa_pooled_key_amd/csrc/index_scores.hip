@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         float part = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) part += wr[i] * fmaxf(acc[i] * f, 0.0f);
-        float tot = part + shfl_xor_f(part, 32);
+        float tot = add_xor32(part);
         if (tot == 0.0f) tot = 0.0f;
         if (half == 0 && have[t]) {
             srow[p] = is_cand ? tot : -INFINITY;
@@ -316,7 +316,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             float part = 0.0f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) part += wr[i] * fmaxf(acc[i] * f, 0.0f);
-            tot = part + shfl_xor_f(part, 32);
+            tot = add_xor32(part);
             if (tot == 0.0f) tot = 0.0f;
         }
         if (half == 0 && slot[t] < P) {

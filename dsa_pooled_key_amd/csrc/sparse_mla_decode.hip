@@ -237,8 +237,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // so nothing is fetched from an empty latent buffer.
     const int pre = kv_rows > 0 ? min(n_ptiles, FP8 ? 2 : 1) : 0;
     for (int t = 0; t < pre; ++t) issue(t);
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) my_last = max(my_last, __shfl_xor(my_last, d, kWave));
+    my_last = (int)wave_reduce_u32((uint32_t)my_last,
+                                   [](uint32_t a, uint32_t c) { return (int)a > (int)c ? a : c; });
     if (lane == 0) last_w[v] = my_last;
     if (tid < 2) rescale_s[tid] = 0;
     // The query rows, ids and table entries have landed (loads complete in order); fp8 also
@@ -332,8 +332,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             x[i] = ok ? (sa[i] + sb[i]) * (sm_scale * sc[i]) : -INFINITY;
             tmax = fmaxf(tmax, x[i]);
         }
-        tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-        tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+        tmax = max_xor32(max_xor16(tmax));
         if (lane < 16) red[v][lane] = tmax;
     };
     auto scores = [&](int t, float (&x)[4], float (&sc)[4]) {
@@ -520,8 +519,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     wait_vm<0>();  // a tile fetched ahead but past the last token still lands in LDS first
     // ---- finish: per-head sums (two waves score each head), then out or the split partial
-    l_run += shfl_xor_f(l_run, 16);
-    l_run += shfl_xor_f(l_run, 32);
+    l_run = add_xor32(add_xor16(l_run));
     __syncthreads();
     if (lane < 16) red[v][lane] = l_run;
     __syncthreads();

@@ -28,6 +28,7 @@ constexpr int kBins = 2 * kThreads;  // value bins of the first stage
 // Token-id expansion of a selection (the expand_selection step), fused into the top-k block.
 struct ExpandArgs {
     int KP, topk, W, tail, B, S, first_key;
+    int vec8;  // KP = 8, W % 4 == 0 and token_ids 16-byte aligned: a pool's slots are two int4
     const int32_t *row_seq;
     const int32_t *row_pos;
     const uint8_t *valid;
@@ -35,7 +36,6 @@ struct ExpandArgs {
 };
 
 constexpr int kMaxMembers = kWave;  // cutoff bins up to this size are ranked by one wave
-constexpr int kStage = 4096;        // selections up to this width are staged in LDS
 
 template <int KPT, bool EXPAND>
 __global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int vec,
@@ -50,7 +50,6 @@ __global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int
     __shared__ uint32_t mem[kMaxMembers];
     __shared__ int n_mem;
     __shared__ uint32_t pick[3];
-    __shared__ int32_t sel_s[kStage];
     const int r = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -98,20 +97,16 @@ __global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int
         kmax = key[i] > kmax ? key[i] : kmax;
         if (key[i] != 0u) kmin = key[i] < kmin ? key[i] : kmin;
     }
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {  // unsigned comparisons throughout
-        nc += (uint32_t)__shfl_xor((int)nc, d, kWave);
-        const uint32_t om = (uint32_t)__shfl_xor((int)kmax, d, kWave);
-        const uint32_t on = (uint32_t)__shfl_xor((int)kmin, d, kWave);
-        kmax = om > kmax ? om : kmax;
-        kmin = on < kmin ? on : kmin;
-    }
+    nc = wave_sum_u32(nc);  // unsigned comparisons throughout
+    kmax = wave_max_u32(kmax);
+    kmin = wave_min_u32(kmin);
     if (lane == 0) {
         red3[0][wave] = nc;
         red3[1][wave] = kmax;
         red3[2][wave] = kmin;
     }
     if (tid == 0) n_mem = 0;
+    for (int i = tid; i < kBins; i += kThreads) bins[i] = 0u;  // used only past this barrier
     __syncthreads();
     int n_cand = 0;
     kmax = 0u;
@@ -140,11 +135,15 @@ __global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int
             const int bn = (int)((ordered_key_value(key) - smin) * inv);
             return bn < 0 ? 0 : (bn >= kBins ? kBins - 1 : bn);
         };
-        for (int i = tid; i < kBins; i += kThreads) bins[i] = 0u;
-        __syncthreads();
+        // Up to 16 keys a thread, their bins stay in registers for the membership test below.
+        constexpr bool kKeepBins = KPT <= 16;
+        int bn[kKeepBins ? KPT : 1];
 #pragma unroll
-        for (int i = 0; i < KPT; ++i)
-            if (key[i] != 0u) atomicAdd(&bins[bin_of(key[i])], 1u);
+        for (int i = 0; i < KPT; ++i) {
+            const int bi = key[i] != 0u ? bin_of(key[i]) : -1;
+            if constexpr (kKeepBins) bn[i] = bi;
+            if (bi >= 0) atomicAdd(&bins[bi], 1u);
+        }
         __syncthreads();
         if (tid < kWave) {
             // Wave 0 scans the bins from the top: lane l holds bins kBins-1-32l down to
@@ -163,12 +162,7 @@ __global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int
             uint32_t sum = 0u;
 #pragma unroll
             for (int q = 0; q < kPerLane; ++q) sum += cnt[q];
-            uint32_t inc = sum;
-#pragma unroll
-            for (int d = 1; d < kWave; d <<= 1) {
-                const uint32_t o = __shfl_up(inc, d, kWave);
-                if (tid >= d) inc += o;
-            }
+            const uint32_t inc = wave_incl_sum(sum);
             uint32_t above = inc - sum;
             const uint32_t kk = (uint32_t)Kw;
             if (above < kk && kk <= inc) {
@@ -187,8 +181,10 @@ __global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int
         uint64_t member = 0u;  // keys of this thread that fall in b*
 #pragma unroll
         for (int i = 0; i < KPT; ++i)
-            if (key[i] != 0u && bin_of(key[i]) == bstar) member |= 1ull << i;
-        __syncthreads();  // pick is rewritten below
+            if ((kKeepBins ? bn[kKeepBins ? i : 0] : (key[i] != 0u ? bin_of(key[i]) : -1)) == bstar)
+                member |= 1ull << i;
+        // pick is rewritten only after the next barrier, which every thread reaches after
+        // reading it above.
         if (members <= kMaxMembers) {
             // Stage 2 (small bin): gather its keys and let one wave rank them exactly.
 #pragma unroll
@@ -230,12 +226,7 @@ __global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int
                     const int d0 = 255 - 4 * tid;
                     const uint32_t c0 = hist[d0], c1 = hist[d0 - 1], c2 = hist[d0 - 2], c3 = hist[d0 - 3];
                     const uint32_t sm = c0 + c1 + c2 + c3;
-                    uint32_t inc = sm;
-#pragma unroll
-                    for (int d = 1; d < kWave; d <<= 1) {
-                        const uint32_t o = __shfl_up(inc, d, kWave);
-                        if (tid >= d) inc += o;
-                    }
+                    const uint32_t inc = wave_incl_sum(sm);
                     const uint32_t abv = inc - sm;
                     const uint32_t kk = (uint32_t)k;
                     if (abv < kk && kk <= inc) {
@@ -285,51 +276,50 @@ __global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int
     }
     int total;
     int o = block_exclusive_scan<kThreads>(gt + take_eq, scratch, &total);
-    const bool staged = Kw <= kStage;
+    // Each thread writes the ids it selects at their output positions and, fused, the token
+    // ids of those pools (slots o*KP .. o*KP+KP-1); positions run in pool order across the
+    // block, so a wave's stores land on neighbouring addresses.
     int32_t *orow = sel + (size_t)r * Kw;
-    int eq_seen = 0;
+    int32_t *trow = EXPAND ? ex.token_ids + (size_t)r * ex.W : nullptr;
+    // The keys this thread selects, as a bit mask: all above thr, then its first take_eq keys
+    // equal to thr; the writes below visit only the set bits.
+    uint64_t smask = 0u, emask = 0u;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-        bool s = key[i] > thr;
-        if (key[i] == thr && key[i] != 0u) {
-            s = eq_seen < take_eq;
-            ++eq_seen;
-        }
-        if (s && o < Kw) {
-            if (staged) sel_s[o] = base + i;
-            else orow[o] = base + i;
-            ++o;
-        }
+        if (key[i] > thr) smask |= 1ull << i;
+        if (key[i] == thr && key[i] != 0u) emask |= 1ull << i;
     }
-    if (!staged) {
-        for (int i = take + tid; i < Kw; i += kThreads) orow[i] = -1;
+    for (int k = 0; k < take_eq; ++k) {
+        smask |= emask & (0ull - emask);
+        emask &= emask - 1ull;
+    }
+    while (smask != 0u && o < Kw) {
+        const int p = base + __builtin_ctzll(smask);
+        smask &= smask - 1ull;
+        orow[o] = p;
         if constexpr (EXPAND) {
-            __syncthreads();
-            int32_t *trow = ex.token_ids + (size_t)r * ex.W;
-            for (int j = tid; j < take; j += kThreads) {
-                const int p = orow[j];
-                for (int t = 0; t < ex.KP; ++t) trow[j * ex.KP + t] = ex.first_key + p * ex.KP + t;
+            const int t0 = ex.first_key + p * ex.KP;
+            int32_t *dst = trow + (size_t)o * ex.KP;
+            if (ex.vec8) {  // KP = 8 and 16-byte aligned slots: two 16-byte stores
+                reinterpret_cast<int4 *>(dst)[0] = int4{t0, t0 + 1, t0 + 2, t0 + 3};
+                reinterpret_cast<int4 *>(dst)[1] = int4{t0 + 4, t0 + 5, t0 + 6, t0 + 7};
+            } else {
+                for (int t = 0; t < ex.KP; ++t) dst[t] = t0 + t;
             }
         }
-    } else {
-        __syncthreads();
-        for (int i = tid; i < Kw; i += kThreads) orow[i] = i < take ? sel_s[i] : -1;
+        ++o;
     }
+    for (int i = take + tid; i < Kw; i += kThreads) orow[i] = -1;
     if constexpr (EXPAND) {
-        // Token slots (as expand_selection): selected pool j fills slots j*KP .. j*KP+KP-1,
-        // then -1 up to topk, then the tail tokens after the last whole pool up to row_pos,
-        // each only if valid.
-        int32_t *trow = ex.token_ids + (size_t)r * ex.W;
+        // The remaining token slots (as expand_selection): -1 up to topk, then the tail tokens
+        // after the last whole pool up to row_pos, each only if valid.
         const int b = ex.row_seq[r];
         const long long pos = ex.row_pos[r];
         const bool tail_ok = ex.tail && b >= 0 && b < ex.B && pos + 1 > ex.first_key;
         const long long start = ex.first_key + ((pos + 1 - ex.first_key) / ex.KP) * ex.KP;
-        for (int i = (staged ? 0 : take * ex.KP) + tid; i < ex.W; i += kThreads) {
+        for (int i = take * ex.KP + tid; i < ex.W; i += kThreads) {
             int v = -1;
-            const int j = i / ex.KP;
-            if (j < take) {
-                v = ex.first_key + sel_s[j] * ex.KP + (i - j * ex.KP);
-            } else if (i >= ex.topk && tail_ok) {
+            if (i >= ex.topk && tail_ok) {
                 const long long t = start + (i - ex.topk);
                 if (t <= pos && t < ex.S && ex.valid[(size_t)b * ex.S + t]) v = (int)t;
             }
@@ -383,7 +373,9 @@ hipError_t launch_topk_expand(int Q, int P, int Kw, const float *scores, const u
     if (Kw == 0)  // nothing to select: the plain expansion writes the -1 row and the tail
         return launch_expand_selection(Q, 0, KP, topk, W, tail, B, S, first_key, P, sel, row_seq,
                                        row_pos, valid, token_ids, stream);
-    const ExpandArgs ex{KP, topk, W, tail ? 1 : 0, B, S, first_key, row_seq, row_pos, valid, token_ids};
+    const int vec8 = KP == 8 && (W & 3) == 0 && (reinterpret_cast<uintptr_t>(token_ids) & 15) == 0;
+    const ExpandArgs ex{KP, topk, W, tail ? 1 : 0, B, S, first_key, vec8, row_seq, row_pos, valid,
+                        token_ids};
     return launch_any(Q, P, Kw, scores, cand, sel, &ex, stream);
 }
 
