@@ -314,6 +314,28 @@ def test_sparse_mla_repeatable_paging_invariant_and_masks_bad_ids():
     o3, l3 = dsa.sparse_mla_decode(cfg, x.q_abs, _dev(tok), x.row_seq, kvp, B=wl.B,
                                    sm_scale=di.sm_scale, S=wl.S, block_table=_dev(table))
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    # the same table padded with unmapped columns past what the kernel stages in LDS (the
+    # lookups then go to global memory): identical bits
+    wide = np.full((wl.B, 9000), -1, np.int32)
+    wide[:, :nb] = table
+    o3w, l3w = dsa.sparse_mla_decode(cfg, x.q_abs, _dev(tok), x.row_seq, kvp, B=wl.B,
+                                     sm_scale=di.sm_scale, S=wl.S, block_table=_dev(wide))
+    assert torch.equal(o1, o3w) and torch.equal(l1, l3w)
+    # a page size that is not a power of two: identical bits
+    bs3 = 48
+    nb3 = (wl.S + bs3 - 1) // bs3
+    table3 = rng.permutation(wl.B * nb3).astype(np.int32).reshape(wl.B, nb3)
+    paged3 = np.zeros((wl.B * nb3 * bs3, 512), np.uint16)
+    for b in range(wl.B):
+        for j in range(nb3):
+            n = min(bs3, wl.S - j * bs3)
+            paged3[table3[b, j] * bs3: table3[b, j] * bs3 + n] = \
+                di.kv[b * wl.S + j * bs3: b * wl.S + j * bs3 + n]
+    kvp3 = torch.from_numpy(paged3.view(np.int16)).cuda().view(torch.bfloat16)
+    o3p, l3p = dsa.sparse_mla_decode(cfg, x.q_abs, _dev(tok), x.row_seq, kvp3, B=wl.B,
+                                     sm_scale=di.sm_scale, S=wl.S, block_table=_dev(table3),
+                                     block_size=bs3)
+    assert torch.equal(o1, o3p) and torch.equal(l1, l3p)
     # ids past the sequence, negative ids and unmapped blocks are skipped like -1
     bad = tok.copy()
     bad[0, 5] = wl.S + 10
