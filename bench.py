@@ -47,10 +47,17 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+KERNEL_HEADERS = {
+    "compact_index_scores": ("dsa_device.hpp", "dsa_score_range.hpp"),
+    "index_scores": ("dsa_device.hpp", "dsa_score_range.hpp"),
+    "topk_expand": ("dsa_device.hpp", "dsa_topk_row.hpp"),
+}
+
+
 def source_hash(kernel: str) -> str:
     path = os.path.join(ROOT, "dsa_pooled_key_amd", "csrc", KERNEL_SOURCES[kernel])
     h = hashlib.sha256(open(path, "rb").read())
-    for dep in ("dsa_device.hpp",):
+    for dep in KERNEL_HEADERS.get(kernel, ("dsa_device.hpp",)):
         h.update(open(os.path.join(ROOT, "dsa_pooled_key_amd", "csrc", dep), "rb").read())
     return h.hexdigest()[:16]
 

@@ -24,20 +24,13 @@
 // score row costs 5 bytes per pool slot.
 #include "dsa_device.hpp"
 #include "dsa_launch.hpp"
+#include "dsa_score_range.hpp"
 
 namespace dsa {
 namespace {
 
 constexpr int kThreads = 256;
 
-// LDS position (in bf16 elements) of the 16-byte chunk c of query head h: the chunks of each
-// head row are XOR-rotated by the head index, so the 16 lanes of one ds_read_b128 pass (heads
-// n..n+15, one chunk each) fall in distinct banks instead of all at the same offset of rows
-// D*2 bytes apart.
-template <int D>
-__device__ __forceinline__ int q_slot(int h, int c) {
-    return h * D + 8 * (c ^ (h & (D / 8 - 1)));
-}
 constexpr int kTilesPerWave = 2;
 constexpr int kChunk = (kThreads / kWave) * kTilesPerWave * 32;
 
@@ -198,15 +191,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 }
 
 // The compaction and the scoring in one launch: block (r, c) takes pool slots
-// [c*chunk, c*chunk + chunk) of row r directly, wave w's tile t being slots
-// c*chunk + (t*4 + w)*32 .. +31, lane n (and its partner n + 32, which holds the other half of
-// the channels) owning slot n of the tile. The validity flags of those slots are read after
-// the row's sequence is known, and a pooled key is requested only for a slot that is valid and
-// whose last token is at or before the row position, so the keys of invalid pools are never
-// read (the saving the compacted id list exists for) and no id list is written or read. Every
-// slot of the chunk is written by its lane: the score and cand = 1 for a candidate, -inf and
-// cand = 0 otherwise. Three dependent round trips, as in the listed form: the row's sequence
-// and query; the flags; the keys.
+// [c*chunk, c*chunk + chunk) of row r directly (score_range).
 template <int D, bool FP8, int TPW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void index_scores_valid_kernel(
     int B, int P, int Hi, int KP, int first_key, float scale, const uint16_t *__restrict__ q,
@@ -214,116 +199,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int32_t *__restrict__ row_pos, const void *__restrict__ keys,
     const float *__restrict__ key_scales, const uint8_t *__restrict__ pool_valid,
     float *__restrict__ scores, uint8_t *__restrict__ cand) {
-    constexpr int kSteps = D / 16;
-    constexpr int kHalf = D / 2;
-    constexpr int kQVec = 32 * D / 8;
-    constexpr int kWaves = kThreads / kWave;
-    constexpr int kChunkV = kWaves * TPW * 32;
+    constexpr int kChunkV = (kThreads / kWave) * TPW * 32;
     __shared__ __attribute__((aligned(16))) uint16_t q_s[32 * D];
     __shared__ float w_s[32];
-
-    const int r = blockIdx.x;
-    const int c = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int n = lane & 31;
-    const int half = lane >> 5;
-    float *srow = scores + (size_t)r * P;
-    uint8_t *crow = cand + (size_t)r * P;
-
-    // Round trip 1: the row's sequence and position, its query and head weights.
-    const int b = row_seq[r];
-    const long long pos = row_pos[r];
-    u32x4 qv[(kQVec + kThreads - 1) / kThreads];
-#pragma unroll
-    for (int k = 0; k < (kQVec + kThreads - 1) / kThreads; ++k) {
-        const int e = (tid + k * kThreads) * 8;
-        const int h = e / D;
-        qv[k] = u32x4{0u, 0u, 0u, 0u};
-        if (e < 32 * D && h < Hi) qv[k] = *reinterpret_cast<const u32x4 *>(q + ((size_t)r * Hi) * D + e);
-    }
-    const float wv = tid < 32 && tid < Hi ? w[(size_t)r * Hi + tid] : 0.0f;
-    const bool row_ok = b >= 0 && b < B;
-    // Pools [0, lim) end at or before the row position (and exist).
-    long long lim = pos + 1 > first_key ? (pos + 1 - first_key) / KP : 0;
-    if (!row_ok) lim = 0;
-    if (lim > P) lim = P;
-
-    // Round trip 2: the validity flags of this lane's slots; round trip 3: their keys.
-    int slot[TPW];
-    bool ok[TPW];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        slot[t] = c * kChunkV + (t * kWaves + wave) * 32 + n;
-        ok[t] = slot[t] < lim && pool_valid[(size_t)b * P + slot[t]] != 0;
-    }
-    u32x4 raw[TPW][FP8 ? kHalf / 16 : kSteps];
-    float ksc[TPW];
-    bool any[TPW];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        // The wave skips a tile with no candidate; otherwise a lane without one fetches nothing
-        // and its column is dropped.
-        any[t] = __builtin_amdgcn_ballot_w64(ok[t]) != 0;
-        ksc[t] = 1.0f;
-#pragma unroll
-        for (int k = 0; k < (FP8 ? kHalf / 16 : kSteps); ++k) raw[t][k] = u32x4{0u, 0u, 0u, 0u};
-        if (ok[t]) {
-            const size_t kr = (size_t)b * P + slot[t];
-            if constexpr (FP8) {
-                const uint8_t *krow = static_cast<const uint8_t *>(keys) + kr * D + half * kHalf;
-#pragma unroll
-                for (int ch = 0; ch < kHalf / 16; ++ch) raw[t][ch] = *reinterpret_cast<const u32x4 *>(krow + ch * 16);
-                ksc[t] = key_scales[kr];
-            } else {
-                const uint16_t *krow = static_cast<const uint16_t *>(keys) + kr * D + half * kHalf;
-#pragma unroll
-                for (int st = 0; st < kSteps; ++st) raw[t][st] = *reinterpret_cast<const u32x4 *>(krow + st * 8);
-            }
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < (kQVec + kThreads - 1) / kThreads; ++k) {
-        const int e = (tid + k * kThreads) * 8;
-        if (e < 32 * D) *reinterpret_cast<u32x4 *>(q_s + q_slot<D>(e / D, (e % D) / 8)) = qv[k];
-    }
-    if (tid < 32) w_s[tid] = wv;
-    __syncthreads();
-
-    float wr[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) wr[i] = w_s[8 * (i >> 2) + 4 * half + (i & 3)];
-
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        float tot = 0.0f;
-        if (any[t]) {
-            f32x16 acc = {};
-#pragma unroll
-            for (int st = 0; st < kSteps; ++st) {
-                u32x4 kb;
-                if constexpr (FP8) {
-                    const u32x4 rw = raw[t][st >> 1];
-                    kb = (st & 1) ? e4m3x8_to_bf16x8(rw.z, rw.w) : e4m3x8_to_bf16x8(rw.x, rw.y);
-                } else {
-                    kb = raw[t][st];
-                }
-                const u32x4 qa = *reinterpret_cast<const u32x4 *>(q_s + q_slot<D>(n, half * (kHalf / 8) + st));
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa), as_bf16x8(kb), acc, 0, 0, 0);
-            }
-            const float f = scale * ksc[t];
-            float part = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) part += wr[i] * fmaxf(acc[i] * f, 0.0f);
-            tot = add_xor32(part);
-            if (tot == 0.0f) tot = 0.0f;
-        }
-        if (half == 0 && slot[t] < P) {
-            srow[slot[t]] = ok[t] ? tot : -INFINITY;
-            crow[slot[t]] = ok[t] ? 1 : 0;
-        }
-    }
+    score_range<D, FP8, TPW, kThreads>(blockIdx.x, blockIdx.y * kChunkV, B, P, Hi, KP, first_key,
+                                       scale, q, w, row_seq, row_pos, keys, key_scales, pool_valid,
+                                       scores, cand, q_s, w_s);
 }
 
 template <int D, bool FP8, int TPW>
