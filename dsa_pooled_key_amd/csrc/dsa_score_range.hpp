@@ -29,6 +29,15 @@ __device__ __forceinline__ int q_slot(int h, int c) {
     return h * D + 8 * (c ^ (h & (D / 8 - 1)));
 }
 
+// Pools [0, limit) of a row at position pos end at or before it (and exist); 0 for a row whose
+// sequence index is outside the batch.
+__device__ __forceinline__ long long row_pool_limit(int b, long long pos, int B, int P, int KP,
+                                                    int first_key) {
+    if (b < 0 || b >= B) return 0;
+    long long lim = pos + 1 > first_key ? (pos + 1 - first_key) / KP : 0;
+    return lim > P ? P : lim;
+}
+
 // q_s: LDS of 32*D bf16 (16-byte aligned); w_s: LDS of 32 floats. Ends with the block's stores
 // issued (not waited for).
 template <int D, bool FP8, int TPW, int NT>
@@ -63,10 +72,7 @@ __device__ __forceinline__ void score_range(
     }
     const float wv = tid < 32 && tid < Hi ? w[(size_t)r * Hi + tid] : 0.0f;
     const bool row_ok = b >= 0 && b < B;
-    // Pools [0, lim) end at or before the row position (and exist).
-    long long lim = pos + 1 > first_key ? (pos + 1 - first_key) / KP : 0;
-    if (!row_ok) lim = 0;
-    if (lim > P) lim = P;
+    const long long lim = row_pool_limit(b, pos, B, P, KP, first_key);
 
     // Round trip 2: the validity flags of this lane's slots; round trip 3: their keys.
     int slot[TPW];

@@ -190,8 +190,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     fill_tail();
 }
 
-// The compaction and the scoring in one launch: block (r, c) takes pool slots
-// [c*chunk, c*chunk + chunk) of row r directly (score_range).
+// The compaction and the scoring in one launch: each block scores one (row, chunk) range of
+// pool slots (score_range). With up to kThreads rows, the blocks are renumbered so that the
+// ranges holding candidates come first, row after row, and the ranges past a row's limit
+// after them: block L takes the L-th range of that order. Consecutive blocks are dispatched to
+// different CUs, so a long row's ranges spread over the chip instead of piling onto the CUs
+// that the plain (row, chunk) grid would give them. The order costs one block scan over the
+// rows' positions, read in the same round trip as the row's own geometry.
 template <int D, bool FP8, int TPW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void index_scores_valid_kernel(
     int B, int P, int Hi, int KP, int first_key, float scale, const uint16_t *__restrict__ q,
@@ -202,9 +207,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     constexpr int kChunkV = (kThreads / kWave) * TPW * 32;
     __shared__ __attribute__((aligned(16))) uint16_t q_s[32 * D];
     __shared__ float w_s[32];
-    score_range<D, FP8, TPW, kThreads>(blockIdx.x, blockIdx.y * kChunkV, B, P, Hi, KP, first_key,
-                                       scale, q, w, row_seq, row_pos, keys, key_scales, pool_valid,
-                                       scores, cand, q_s, w_s);
+    __shared__ int scan_s[kThreads / kWave + 1];
+    __shared__ int item_s[2];
+    const int Q = gridDim.x, chunks = gridDim.y;
+    int r = blockIdx.x, c = blockIdx.y;
+    if (Q <= kThreads && Q * chunks < (1 << 15)) {
+        const int t = threadIdx.x;
+        const int L = blockIdx.y * Q + blockIdx.x;
+        if (t == 0) item_s[0] = r, item_s[1] = c;  // (ordered before the finder by the scan)
+        int act = 0;  // ranges of row t holding candidates
+        if (t < Q) {
+            const long long lim = row_pool_limit(row_seq[t], row_pos[t], B, P, KP, first_key);
+            act = (int)((lim + kChunkV - 1) / kChunkV);
+        }
+        const int idle = t < Q ? chunks - act : 0;
+        int tot;  // both counts in one scan (each sum is below Q * chunks < 2^15)
+        const int pre = block_exclusive_scan<kThreads>(act | (idle << 15), scan_s, &tot);
+        const int pa = pre & 0x7fff, pi = pre >> 15, n_act = tot & 0x7fff;
+        if (t < Q) {
+            if (L < n_act) {
+                if (L >= pa && L < pa + act) item_s[0] = t, item_s[1] = L - pa;
+            } else if (L - n_act >= pi && L - n_act < pi + idle) {
+                item_s[0] = t, item_s[1] = act + (L - n_act - pi);
+            }
+        }
+        __syncthreads();
+        r = min(max(item_s[0], 0), Q - 1);
+        c = min(max(item_s[1], 0), chunks - 1);
+    }
+    score_range<D, FP8, TPW, kThreads>(r, c * kChunkV, B, P, Hi, KP, first_key, scale, q, w,
+                                       row_seq, row_pos, keys, key_scales, pool_valid, scores,
+                                       cand, q_s, w_s);
 }
 
 template <int D, bool FP8, int TPW>
