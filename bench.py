@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFS = 2500.0         # MI355X dense bf16 MFMA, TFLOP/s
 MALL_BYTES = 256 << 20         # Infinity Cache
 KERNEL_SOURCES = {
     "compact_index_scores": "index_scores.hip",
@@ -100,6 +101,103 @@ def algorithmic_bytes(di, n_valid, n_tokens):
 
 
 # ---------------------------------------------------------------- GPU part
+
+def cycle_percentiles(cycle_graph, reps, n_cycles, stream):
+    """p10 / p50 / p90 of the per-step time over n_cycles replays of the replica cycle, each
+    bracketed by its own HIP events on the replay stream."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_cycles)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        cycle_graph.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) / reps for a, b in ev])
+    return {f"p{q}": round(float(np.percentile(t, q)), 5) for q in (10, 50, 90)}
+
+
+def run_chain(name, steps, warmup, seed=0, replicas=0):
+    """The whole chain on another workload: ms per step over HIP-graph replays of a cycle of
+    input replicas (at least 1 GiB of distinct inputs), plus what the rooflines need."""
+    import torch
+
+    from dsa_pooled_key_amd import synth
+    from dsa_pooled_key_amd.pipeline import DecodeStep, DeviceDecodeInputs
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    di = synth.make_decode_inputs(name, seed=seed)
+    wl = di.wl
+    x0 = DeviceDecodeInputs.upload(di, dev)
+    probe = DecodeStep(wl, x0, di.scale, di.sm_scale)
+    probe.run()
+    torch.cuda.synchronize()
+    n_tokens = int((probe.token_ids >= 0).sum().item())
+    n_cand = int(probe.cand.sum(dtype=torch.int64).item())
+    n_valid = (di.pool_valid != 0).sum(axis=1)
+    alg = algorithmic_bytes(di, n_valid, n_tokens)
+    reps = replicas or int(min(16, max(2, -(-4 * MALL_BYTES // alg["step"]))))
+    xs = [x0] + [DeviceDecodeInputs(**{k: (None if v is None else v.clone())
+                                       for k, v in x0.__dict__.items()}) for _ in range(reps - 1)]
+    stps = [probe] + [DecodeStep(wl, x, di.scale, di.sm_scale) for x in xs[1:]]
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    for i in range(max(warmup, reps)):
+        stps[i % reps].run()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for st in stps:
+            st.run()
+    n_cycles = max(2, -(-steps // reps))
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n_cycles):
+        g.replay()
+    b.record(stream)
+    b.synchronize()
+    ms = a.elapsed_time(b) / (n_cycles * reps)
+    torch.cuda.set_stream(torch.cuda.default_stream())
+    log(f"{name}: {ms * 1e3:.2f} us per step over {n_cycles * reps} steps, {reps} replicas "
+        f"(inputs drawn and uploaded in {time.time() - t0:.1f}s)")
+    out = {"di": di, "alg": alg, "ms": ms, "reps": reps, "steps": n_cycles * reps,
+           "n_tokens": n_tokens, "n_cand": n_cand}
+    del stps, xs, x0, probe, g
+    torch.cuda.empty_cache()
+    return out
+
+
+def extra_lines(args):
+    """X128 decode and C4 prefill, reported beside the main line."""
+    extra = {}
+    if not args.no_x128:
+        r = run_chain("decode_b8_128k", args.extra_steps, args.warmup, args.seed)
+        wl = r["di"].wl
+        gbs = r["alg"]["step"] / (r["ms"] * 1e-3) / 1e9
+        extra["x128"] = {
+            "workload": f"{wl.name}: {wl.Q} decode queries, every context {wl.S}, kpool {wl.kpool}, "
+                        f"topk {wl.topk}, bf16 keys and latent, contiguous",
+            "queries_per_s": round(wl.Q / (r["ms"] * 1e-3), 1), "ms_per_step": round(r["ms"], 5),
+            "steps": r["steps"], "replicas": r["reps"],
+            "algorithmic_bytes": r["alg"]["step"], "achieved_GBs": round(gbs, 1),
+            "frac_of_peak_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+    if not args.no_prefill:
+        r = run_chain("prefill_2048_64k", args.extra_steps, args.warmup, args.seed)
+        wl = r["di"].wl
+        flop = 2 * wl.index_heads * wl.index_dim * r["n_cand"] + 4 * wl.heads * 512 * r["n_tokens"]
+        tfs = flop / (r["ms"] * 1e-3) / 1e12
+        extra["prefill"] = {
+            "workload": f"{wl.name}: {wl.Q} causal rows at positions {wl.S - wl.Q}..{wl.S - 1} of "
+                        f"one {wl.S}-token sequence, kpool {wl.kpool}, topk {wl.topk}, bf16",
+            "rows_per_s": round(wl.Q / (r["ms"] * 1e-3), 1), "ms_per_step": round(r["ms"], 5),
+            "steps": r["steps"], "replicas": r["reps"],
+            "flop": flop, "candidate_pools": r["n_cand"], "tokens_attended": r["n_tokens"],
+            "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": PEAK_BF16_TFS,
+                         "unit": "TFLOP/s", "frac": round(tfs / PEAK_BF16_TFS, 4)}}
+    return extra
 
 def run_gpu(args):
     import torch
@@ -170,6 +268,7 @@ def run_gpu(args):
 
     ms_step = timed(g_cycle, g_single, args.steps)
     log(f"decode step: {ms_step * 1e3:.2f} us ({wl.Q / ms_step * 1e3:.0f} queries/s)")
+    pct = cycle_percentiles(g_cycle, reps, max(8, args.steps // reps), stream)
 
     # Per-stage durations: each stage alone, same replicas, same graph replay.
     stage_fns = {
@@ -212,7 +311,7 @@ def run_gpu(args):
     torch.cuda.set_stream(torch.cuda.default_stream())
 
     return {
-        "di": di, "alg": alg, "ms_step": ms_step, "stage_us": stage_us, "reps": reps,
+        "di": di, "alg": alg, "ms_step": ms_step, "pct": pct, "stage_us": stage_us, "reps": reps,
         "n_tokens": n_tokens, "kpool": {"us": kp_us, "tokens": kp_tokens, "bytes": kp_bytes,
                                         "batch": kb},
     }
@@ -310,6 +409,10 @@ def main():
     ap.add_argument("--kpool-batch", type=int, default=8)
     ap.add_argument("--cpu-sample-every", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-x128", action="store_true", help="skip the X128 decode line")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the C4 prefill line")
+    ap.add_argument("--extra-steps", type=int, default=60,
+                    help="timed steps of the X128 and prefill lines")
     ap.add_argument("--eager", choices=["all", "select", "attend"], default=None,
                     help="profiling mode: eager launches only, no timing report")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -338,6 +441,7 @@ def main():
     traffic = measured_traffic(dom, wl.name)
     step_gbs = alg["step"] / (ms * 1e-3) / 1e9
 
+    extra = extra_lines(args)
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
@@ -352,6 +456,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "ms_per_step_pct": res["pct"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -395,6 +500,7 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    line.update(extra)
     print(json.dumps(line), flush=True)
 
 

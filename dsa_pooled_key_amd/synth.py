@@ -15,6 +15,7 @@ size):
 * ``decode_b8_32k``   8 queries, 32,768 slots, lengths U[16K, 32K], kpool 4, topk 2,048.
 * ``decode_b4_256k``  4 queries at 262,144 tokens, paged bf16 latent in a shuffled block table.
 * ``prefill_2048_64k`` 2,048 causal rows at positions 63,488..65,535 of a 65,536-token context.
+* ``decode_b8_128k``  8 queries, every sequence at 131,072 tokens, otherwise decode_b8_32k.
 * ``fp8_mixed_b32``   32 queries, log-uniform lengths in [4K, 131,072], kpool 8, topk 4,096,
   fp8 pooled keys and fp8 paged latent with per-row f32 scales, ~5% of slots invalid.
 
@@ -185,6 +186,10 @@ WORKLOADS = {
                                index_heads=32, index_dim=128, heads=32, paged=True),
     "prefill_2048_64k": Workload("prefill_2048_64k", B=1, S=65536, Q=2048, kpool=4, topk=2048,
                                  index_heads=32, index_dim=128, heads=32, rows="prefill_tail"),
+    # Decode at a full 131,072-token context: decode_b8_32k's recipe with every sequence at
+    # S (bench line "x128"; the same kernels and shapes as the parity-tested workloads).
+    "decode_b8_128k": Workload("decode_b8_128k", B=8, S=131072, Q=8, kpool=4, topk=2048,
+                               index_heads=32, index_dim=128, heads=32),
     "fp8_mixed_b32": Workload("fp8_mixed_b32", B=32, S=131072, Q=32, kpool=8, topk=4096,
                               index_heads=32, index_dim=128, heads=32, key_fp8=True,
                               kv_fp8=True, paged=True, lengths="loguniform", invalid_rate=0.05),
