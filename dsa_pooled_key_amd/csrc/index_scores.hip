@@ -240,6 +240,146 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                                        cand, q_s, w_s);
 }
 
+// Rows that all read one sequence's keys (prefill: consecutive positions of one sequence), as
+// a blocked product: block (g, c) scores rows 8g..8g+7 against pools [128c, 128c + 128). The
+// pools' keys are copied once into LDS (each row's 16-byte chunks XOR-rotated by the pool
+// index, so the 16 lanes of a fragment read fall in distinct banks) and reused by all 8 rows;
+// wave w keeps the query fragments of rows 8g+2w and 8g+2w+1 in registers and runs, for each
+// 32-pool tile, the two rows' 32-head x 32-pool products on v_mfma_f32_32x32x16_bf16 from the
+// same key fragments. Candidacy (the pool's flag and the row's causal limit) and the
+// relu-weighted head sum are the epilogue, as in the per-row form. One round trip: flags, keys,
+// queries, weights and positions are requested together.
+constexpr int kRB = 8;    // rows a block
+constexpr int kCB = 128;  // pools a block
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void index_scores_rowblock_kernel(
+    int Q, int P, int Hi, int KP, int first_key, float scale, const uint16_t *__restrict__ q,
+    const float *__restrict__ w, const int32_t *__restrict__ row_seq,
+    const int32_t *__restrict__ row_pos, const void *__restrict__ keys,
+    const float *__restrict__ key_scales, const uint8_t *__restrict__ pool_valid,
+    float *__restrict__ scores, uint8_t *__restrict__ cand) {
+    constexpr int kSteps = D / 16;
+    constexpr int kRowBytes = FP8 ? D : 2 * D;     // one pool's key row
+    constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks a key row
+    constexpr int kPieces = kCB * kChunks / kThreads;  // chunks a thread copies
+    static_assert(kPieces >= 1 && kCB * kChunks % kThreads == 0, "key tile split");
+    __shared__ __attribute__((aligned(16))) uint8_t ktile[kCB * kRowBytes];
+    __shared__ float w_s[kRB][32];
+    __shared__ float ks_s[kCB];
+    __shared__ int lim_s[kRB];
+
+    const int g = blockIdx.x, c = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int n = lane & 31;
+    const int half = lane >> 5;
+    const int p0 = c * kCB;
+    auto kpos = [&](int p, int ch) { return p * kRowBytes + 16 * (ch ^ (p & (kChunks - 1))); };
+
+    // One round trip. Key chunks (pools past P read pool P-1, never used):
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) {
+        const int e = tid + k * kThreads;  // chunk e % kChunks of pool e / kChunks
+        const int p = e / kChunks, ch = e % kChunks;
+        const int pg = min(p0 + p, P - 1);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(keys) +
+                                                         (size_t)pg * kRowBytes + 16 * ch);
+        *reinterpret_cast<u32x4 *>(ktile + kpos(p, ch)) = v;
+    }
+    if (FP8 && tid < kCB) ks_s[tid] = key_scales[min(p0 + tid, P - 1)];
+    // Rows, weights and limits of the block's rows (a row outside [0, Q) or of no sequence of
+    // the batch has no candidate).
+    if (tid < kRB * 32) {
+        const int rl = tid / 32, h = tid % 32, r = g * kRB + rl;
+        w_s[rl][h] = r < Q && h < Hi ? w[(size_t)r * Hi + h] : 0.0f;
+        if (h == 0)
+            lim_s[rl] = r < Q ? (int)row_pool_limit(row_seq[r], row_pos[r], 1, P, KP, first_key) : 0;
+    }
+    // Flags of this lane's pools (tile t: pool p0 + 32t + n).
+    bool flag[kCB / 32];
+#pragma unroll
+    for (int t = 0; t < kCB / 32; ++t) {
+        const int p = p0 + 32 * t + n;
+        flag[t] = p < P && pool_valid[p] != 0;
+    }
+    // Query fragments of the wave's two rows (A operand: head n, channels half*D/2 + 8st ..).
+    const int r0 = g * kRB + 2 * wave;
+    u32x4 qa[2][kSteps];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int r = min(r0 + j, Q - 1);
+        const int h = min(n, Hi - 1);
+        const u32x4 *qrow = reinterpret_cast<const u32x4 *>(q + ((size_t)r * Hi + h) * D + half * (D / 2));
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) qa[j][st] = qrow[st];
+    }
+    __syncthreads();
+    if (n >= Hi) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int st = 0; st < kSteps; ++st) qa[j][st] = u32x4{0u, 0u, 0u, 0u};
+    }
+    const int lim0 = lim_s[2 * wave], lim1 = lim_s[2 * wave + 1];
+
+#pragma unroll
+    for (int t = 0; t < kCB / 32; ++t) {
+        const int pl = 32 * t + n;  // pool of this lane within the tile block
+        f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+            u32x4 kb;
+            if constexpr (FP8) {  // 16 fp8 channels feed two steps
+                const u32x4 raw = *reinterpret_cast<const u32x4 *>(
+                    ktile + kpos(pl, half * (D / 32) + (st >> 1)));
+                kb = (st & 1) ? e4m3x8_to_bf16x8(raw.z, raw.w) : e4m3x8_to_bf16x8(raw.x, raw.y);
+            } else {
+                kb = *reinterpret_cast<const u32x4 *>(ktile + kpos(pl, half * (D / 16) + st));
+            }
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[0][st]), as_bf16x8(kb), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[1][st]), as_bf16x8(kb), acc1, 0, 0, 0);
+        }
+        const float f = FP8 ? scale * ks_s[pl] : scale;
+        float part0 = 0.0f, part1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int h = 8 * (i >> 2) + 4 * half + (i & 3);
+            part0 += w_s[2 * wave][h] * fmaxf(acc0[i] * f, 0.0f);
+            part1 += w_s[2 * wave + 1][h] * fmaxf(acc1[i] * f, 0.0f);
+        }
+        float tot0 = add_xor32(part0), tot1 = add_xor32(part1);
+        if (tot0 == 0.0f) tot0 = 0.0f;
+        if (tot1 == 0.0f) tot1 = 0.0f;
+        const int p = p0 + pl;
+        if (half == 0 && p < P) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int r = r0 + j;
+                if (r < Q) {
+                    const bool ok = flag[t] && p < (j ? lim1 : lim0);
+                    scores[(size_t)r * P + p] = ok ? (j ? tot1 : tot0) : -INFINITY;
+                    cand[(size_t)r * P + p] = ok ? 1 : 0;
+                }
+            }
+        }
+    }
+}
+
+template <int D, bool FP8>
+hipError_t launch_rowblock_d(int Q, int P, int Hi, int KP, int first_key, float scale,
+                             const uint16_t *q, const float *w, const int32_t *row_seq,
+                             const int32_t *row_pos, const void *keys, const float *key_scales,
+                             const uint8_t *pool_valid, float *scores, uint8_t *cand,
+                             hipStream_t stream) {
+    hipLaunchKernelGGL((index_scores_rowblock_kernel<D, FP8>),
+                       dim3((Q + kRB - 1) / kRB, (P + kCB - 1) / kCB), dim3(kThreads), 0, stream,
+                       Q, P, Hi, KP, first_key, scale, q, w, row_seq, row_pos, keys, key_scales,
+                       pool_valid, scores, cand);
+    return hipGetLastError();
+}
+
 template <int D, bool FP8, int TPW>
 hipError_t launch_valid_d(int Q, int B, int P, int Hi, int KP, int first_key, float scale,
                           const uint16_t *q, const float *w, const int32_t *row_seq,
@@ -298,6 +438,21 @@ hipError_t launch_index_scores_valid(int Q, int B, int P, int Hi, int D, int KP,
                                      const uint8_t *pool_valid, float *scores, uint8_t *cand,
                                      hipStream_t stream) {
     if (Q == 0 || P == 0) return hipSuccess;
+    // Many rows of one sequence (prefill): the row-blocked product, keys read once per 8 rows.
+    if (B == 1 && Q >= kRB) {
+#define DSA_ISR_CASE(d)                                                                         \
+        if (D == d)                                                                             \
+            return key_fp8 ? launch_rowblock_d<d, true>(Q, P, Hi, KP, first_key, scale, q, w,   \
+                                                        row_seq, row_pos, keys, key_scales,     \
+                                                        pool_valid, scores, cand, stream)       \
+                           : launch_rowblock_d<d, false>(Q, P, Hi, KP, first_key, scale, q, w,  \
+                                                         row_seq, row_pos, keys, key_scales,    \
+                                                         pool_valid, scores, cand, stream);
+        DSA_ISR_CASE(32)
+        DSA_ISR_CASE(64)
+        DSA_ISR_CASE(128)
+#undef DSA_ISR_CASE
+    }
     // fp8 keys leave registers for four tiles a wave (512 pool slots a block); bf16 keys take
     // twice the registers, so two.
 #define DSA_ISV_CASE(d)                                                                          \

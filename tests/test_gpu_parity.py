@@ -183,6 +183,44 @@ def test_compact_index_scores_equals_the_two_calls(name):
     assert np.array_equal(s1.cpu().numpy().view(np.uint32), s2.cpu().numpy().view(np.uint32))
 
 
+@pytest.mark.parametrize("name", ["ragged_prefill", "ragged_fp8"])
+def test_compact_index_scores_rows_of_one_sequence(name):
+    """Many rows over one sequence take the row-blocked scorer (8 rows x 128 pools a block):
+    21 rows (a ragged row group) at random positions, some before first_key, one outside the
+    batch, against the oracle; the pool count is not a multiple of 128."""
+    di, x, _, _ = case(name)
+    wl = di.wl
+    assert wl.pools % 128 != 0
+    rng = np.random.default_rng(11)
+    R = 21
+    src = rng.integers(0, wl.Q, size=R)
+    q, w = di.q[src], di.w[src]
+    row_seq = np.zeros(R, np.int32)
+    row_seq[5] = -1
+    row_pos = rng.integers(0, wl.S, size=R).astype(np.int32)
+    row_pos[:3] = [wl.first_key - 1, wl.first_key + wl.kpool // 2, wl.S - 1]
+    keys1, pv1 = di.keys[:1], di.pool_valid[:1]
+    ks1 = None if di.key_scales is None else di.key_scales[:1]
+    ids, nv = oracle.compact_pools(pv1)
+    cfg = config_for(wl)
+    keys_dev = x.keys[:1].contiguous()
+    scores, cand = dsa.compact_index_scores(
+        cfg, _dev(q.view(np.int16)).view(torch.bfloat16), _dev(w), _dev(row_seq), _dev(row_pos),
+        keys_dev,
+        _dev(pv1), first_key=wl.first_key, scale=di.scale,
+        key_scales=None if ks1 is None else _dev(ks1))
+    gs, gc = scores.cpu().numpy(), cand.cpu().numpy()
+    assert not gc[5].any() and np.all(np.isneginf(gs[5]))
+    ok = np.array([i for i in range(R) if i != 5])
+    rs, rc = oracle.index_scores(q[ok], w[ok], row_seq[ok], row_pos[ok], keys1, ids, nv,
+                                 kpool=wl.kpool, first_key=wl.first_key, scale=di.scale,
+                                 key_scales=ks1)
+    assert np.array_equal(gc[ok], rc)
+    assert rc[0].sum() == 0 and rc[2].sum() == nv[0]
+    assert np.all(np.isneginf(gs[ok][rc == 0]))
+    _check_scores(gs[ok], rs, rc)
+
+
 def test_compact_index_scores_edge_rows():
     """Rows outside the batch, a position before first_key, a position in the middle of a pool
     over a sequence whose flags are all nonzero (not only 1), a sequence with no valid pool;
