@@ -114,6 +114,39 @@ __device__ __forceinline__ float add_xor32(float v) {
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// ------------------------------------------------------------------ HBM -> LDS copies
+// One 16-byte-a-lane global -> LDS copy (global_load_lds_dwordx4): lane l's 16 bytes land
+// at lds_base + 16*l. Issued as inline assembly without a memory clobber, so the compiler
+// neither orders nearby LDS reads behind it nor waits for it: it only writes a stage that no
+// code reads before the explicit vmcnt wait and block barrier that publish it (loads complete
+// in order, so the compiler's own waits for other loads stay correct).
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_base), "v"(src)
+                 : "m0");
+}
+
+// Same for 4 bytes a lane (global_load_lds_dword): lane l's dword lands at lds_base + 4*l.
+__device__ __forceinline__ void dma4(const void *src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :
+                 : "s"(lds_base), "v"(src)
+                 : "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)(p);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+// The builtin form lets the compiler's own wait insertion see these waits.
+template <int N>
+__device__ __forceinline__ void wait_vm() {  // at most N vector-memory loads outstanding
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // ------------------------------------------------------------------ wave primitives (DPP)
 // Cross-lane steps through DPP (the VALU reads a neighbour lane's register in the same
 // instruction), not through LDS: GFX9 controls quad_perm, row_shr:n, row_ror:n (rows are 16

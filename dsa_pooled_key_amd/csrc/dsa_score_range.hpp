@@ -38,6 +38,17 @@ __device__ __forceinline__ long long row_pool_limit(int b, long long pos, int B,
     return lim > P ? P : lim;
 }
 
+// One lane's share of a pool's score: sum_i w_i * relu(f * acc_i) = f * sum_i w_i * clamp(acc_i),
+// clamp = max(., 0) for f >= 0 and min(., 0) for f < 0 (one v_med3 against 0 and +-inf), so the
+// scale multiplies once per pool instead of once per head.
+__device__ __forceinline__ float relu_weighted(const f32x16 &acc, const float (&wr)[16], float f) {
+    const float bound = f >= 0.0f ? INFINITY : -INFINITY;
+    float part = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) part += wr[i] * __builtin_amdgcn_fmed3f(acc[i], 0.0f, bound);
+    return part;
+}
+
 // q_s: LDS of 32*D bf16 (16-byte aligned); w_s: LDS of 32 floats. Ends with the block's stores
 // issued (not waited for).
 template <int D, bool FP8, int TPW, int NT>
@@ -137,10 +148,7 @@ __device__ __forceinline__ void score_range(
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa), as_bf16x8(kb), acc, 0, 0, 0);
             }
             const float f = scale * ksc[t];
-            float part = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) part += wr[i] * fmaxf(acc[i] * f, 0.0f);
-            tot = add_xor32(part);
+            tot = f * add_xor32(relu_weighted(acc, wr, f));
             if (tot == 0.0f) tot = 0.0f;
         }
         if (half == 0 && slot[t] < P) {

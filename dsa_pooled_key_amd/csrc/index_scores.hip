@@ -177,10 +177,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa), as_bf16x8(kb), acc, 0, 0, 0);
         }
         const float f = scale * ksc[t];
-        float part = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) part += wr[i] * fmaxf(acc[i] * f, 0.0f);
-        float tot = add_xor32(part);
+        float tot = f * add_xor32(relu_weighted(acc, wr, f));
         if (tot == 0.0f) tot = 0.0f;
         if (half == 0 && have[t]) {
             srow[p] = is_cand ? tot : -INFINITY;
@@ -241,81 +238,105 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 }
 
 // Rows that all read one sequence's keys (prefill: consecutive positions of one sequence), as
-// a blocked product: block (g, c) scores rows 8g..8g+7 against pools [128c, 128c + 128). The
-// pools' keys are copied once into LDS (each row's 16-byte chunks XOR-rotated by the pool
-// index, so the 16 lanes of a fragment read fall in distinct banks) and reused by all 8 rows;
-// wave w keeps the query fragments of rows 8g+2w and 8g+2w+1 in registers and runs, for each
-// 32-pool tile, the two rows' 32-head x 32-pool products on v_mfma_f32_32x32x16_bf16 from the
-// same key fragments. Candidacy (the pool's flag and the row's causal limit) and the
-// relu-weighted head sum are the epilogue, as in the per-row form. One round trip: flags, keys,
-// queries, weights and positions are requested together.
-constexpr int kRB = 8;    // rows a block
-constexpr int kCB = 128;  // pools a block
+// a blocked product: block (g, c) scores rows 8g..8g+7 against pools [2048c, 2048c + 2048) in
+// sixteen tiles of 128 pools. A tile's keys are copied HBM->LDS (global_load_lds_dwordx4, each
+// pool row's 16-byte chunks XOR-rotated by the pool index so the 16 lanes of a fragment read
+// fall in distinct banks) into one of two buffers while the other is multiplied, and reused by
+// all 8 rows; wave w keeps the query fragments of rows 8g+2w and 8g+2w+1 in registers for the
+// whole block and runs, per 32-pool sub-tile, the two rows' 32-head x 32-pool products on
+// v_mfma_f32_32x32x16_bf16 from the same key fragments. Candidacy (the pool's flag and the
+// row's causal limit) and the relu-weighted head sum are the epilogue, as in the per-row form;
+// a tile's results are stored at the start of the next iteration, ahead of that iteration's
+// copies, so the wait that ends it finds them done.
+constexpr int kRB = 8;      // rows a block
+constexpr int kCB = 128;    // pools a key tile
+constexpr int kTiles = 16;  // key tiles a block
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void index_scores_rowblock_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void index_scores_rowblock_kernel(
     int Q, int P, int Hi, int KP, int first_key, float scale, const uint16_t *__restrict__ q,
     const float *__restrict__ w, const int32_t *__restrict__ row_seq,
     const int32_t *__restrict__ row_pos, const void *__restrict__ keys,
     const float *__restrict__ key_scales, const uint8_t *__restrict__ pool_valid,
     float *__restrict__ scores, uint8_t *__restrict__ cand) {
     constexpr int kSteps = D / 16;
-    constexpr int kRowBytes = FP8 ? D : 2 * D;     // one pool's key row
-    constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks a key row
-    constexpr int kPieces = kCB * kChunks / kThreads;  // chunks a thread copies
-    static_assert(kPieces >= 1 && kCB * kChunks % kThreads == 0, "key tile split");
-    __shared__ __attribute__((aligned(16))) uint8_t ktile[kCB * kRowBytes];
+    constexpr int kRowBytes = FP8 ? D : 2 * D;       // one pool's key row
+    constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks a key row
+    constexpr int kTileBytes = kCB * kRowBytes;
+    constexpr int kCopies = kTileBytes / 1024;       // wave-wide 1 KiB copies a tile
+    constexpr int kCopiesPerWave = kCopies / (kThreads / kWave);
+    static_assert(kCopies % (kThreads / kWave) == 0 && kCopiesPerWave >= 1, "tile copies");
+    constexpr int kSub = kCB / 32;                   // 32-pool sub-tiles a tile
+    __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kTileBytes];
+    __shared__ __attribute__((aligned(16))) float ks_s[2][kCB];
     __shared__ float w_s[kRB][32];
-    __shared__ float ks_s[kCB];
     __shared__ int lim_s[kRB];
+    __shared__ __attribute__((aligned(16))) uint8_t fl_s[kCB * kTiles];
 
-    const int g = blockIdx.x, c = blockIdx.y;
+    const int g = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     const int n = lane & 31;
     const int half = lane >> 5;
-    const int p0 = c * kCB;
+    const int pbase = blockIdx.y * kCB * kTiles;
+    const int ntiles = min(kTiles, (P - pbase + kCB - 1) / kCB);
+    const uint8_t *kb8 = static_cast<const uint8_t *>(keys);
     auto kpos = [&](int p, int ch) { return p * kRowBytes + 16 * (ch ^ (p & (kChunks - 1))); };
 
-    // One round trip. Key chunks (pools past P read pool P-1, never used):
+    // Copy of tile it into buffer it&1: copy d of the tile lands at byte 1024d, lane l's 16
+    // bytes at pool row (1024d + 16l) / kRowBytes, chunk position j; the lane fetches the
+    // source chunk that belongs at j. Pools past P read pool P-1 (never used).
+    auto issue_tile = [&](int it) {
+        const int p0 = pbase + it * kCB;
 #pragma unroll
-    for (int k = 0; k < kPieces; ++k) {
-        const int e = tid + k * kThreads;  // chunk e % kChunks of pool e / kChunks
-        const int p = e / kChunks, ch = e % kChunks;
-        const int pg = min(p0 + p, P - 1);
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(keys) +
-                                                         (size_t)pg * kRowBytes + 16 * ch);
-        *reinterpret_cast<u32x4 *>(ktile + kpos(p, ch)) = v;
-    }
-    if (FP8 && tid < kCB) ks_s[tid] = key_scales[min(p0 + tid, P - 1)];
-    // Rows, weights and limits of the block's rows (a row outside [0, Q) or of no sequence of
-    // the batch has no candidate).
+        for (int k = 0; k < kCopiesPerWave; ++k) {
+            const int d = wave * kCopiesPerWave + k;
+            const int p = (1024 * d + 16 * lane) / kRowBytes;
+            const int j = lane % kChunks;
+            const int pg = min(p0 + p, P - 1);
+            dma16(kb8 + (size_t)pg * kRowBytes + 16 * (j ^ (p & (kChunks - 1))),
+                  __builtin_amdgcn_readfirstlane(lds_offset(&ktile[it & 1][1024 * d])));
+        }
+        if constexpr (FP8) {
+            if (wave < kCB / kWave)
+                dma4(key_scales + min(p0 + kWave * wave + lane, P - 1),
+                     __builtin_amdgcn_readfirstlane(lds_offset(&ks_s[it & 1][kWave * wave])));
+        }
+    };
+    // Flags of this lane's pools of tile it (sub-tile t: pool 32t + n), as a bit mask, from the
+    // block's flags in LDS.
+    auto load_flags = [&](int it) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int t = 0; t < kSub; ++t) m |= fl_s[it * kCB + 32 * t + n] != 0 ? 1u << t : 0u;
+        return m;
+    };
+
+    // Prologue, one round trip: tile 0, its flags, the two rows' query fragments, the rows'
+    // weights and limits (a row outside [0, Q) or of no sequence of the batch has none).
+    issue_tile(0);
+    // The block's flags (flags past P read as 0).
+    for (int i = tid; i < kCB * kTiles; i += kThreads) fl_s[i] = pbase + i < P ? pool_valid[pbase + i] : 0;
     if (tid < kRB * 32) {
         const int rl = tid / 32, h = tid % 32, r = g * kRB + rl;
         w_s[rl][h] = r < Q && h < Hi ? w[(size_t)r * Hi + h] : 0.0f;
         if (h == 0)
             lim_s[rl] = r < Q ? (int)row_pool_limit(row_seq[r], row_pos[r], 1, P, KP, first_key) : 0;
     }
-    // Flags of this lane's pools (tile t: pool p0 + 32t + n).
-    bool flag[kCB / 32];
-#pragma unroll
-    for (int t = 0; t < kCB / 32; ++t) {
-        const int p = p0 + 32 * t + n;
-        flag[t] = p < P && pool_valid[p] != 0;
-    }
-    // Query fragments of the wave's two rows (A operand: head n, channels half*D/2 + 8st ..).
     const int r0 = g * kRB + 2 * wave;
     u32x4 qa[2][kSteps];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int r = min(r0 + j, Q - 1);
-        const int h = min(n, Hi - 1);
-        const u32x4 *qrow = reinterpret_cast<const u32x4 *>(q + ((size_t)r * Hi + h) * D + half * (D / 2));
+        const u32x4 *qrow = reinterpret_cast<const u32x4 *>(
+            q + ((size_t)r * Hi + min(n, Hi - 1)) * D + half * (D / 2));
 #pragma unroll
         for (int st = 0; st < kSteps; ++st) qa[j][st] = qrow[st];
     }
+    wait_vm<0>();
     __syncthreads();
+    uint32_t fl_next = load_flags(0);
     if (n >= Hi) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -323,48 +344,83 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             for (int st = 0; st < kSteps; ++st) qa[j][st] = u32x4{0u, 0u, 0u, 0u};
     }
     const int lim0 = lim_s[2 * wave], lim1 = lim_s[2 * wave + 1];
-
+    float wr0[16], wr1[16];
 #pragma unroll
-    for (int t = 0; t < kCB / 32; ++t) {
-        const int pl = 32 * t + n;  // pool of this lane within the tile block
-        f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-        for (int st = 0; st < kSteps; ++st) {
-            u32x4 kb;
-            if constexpr (FP8) {  // 16 fp8 channels feed two steps
-                const u32x4 raw = *reinterpret_cast<const u32x4 *>(
-                    ktile + kpos(pl, half * (D / 32) + (st >> 1)));
-                kb = (st & 1) ? e4m3x8_to_bf16x8(raw.z, raw.w) : e4m3x8_to_bf16x8(raw.x, raw.y);
-            } else {
-                kb = *reinterpret_cast<const u32x4 *>(ktile + kpos(pl, half * (D / 16) + st));
-            }
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[0][st]), as_bf16x8(kb), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[1][st]), as_bf16x8(kb), acc1, 0, 0, 0);
-        }
-        const float f = FP8 ? scale * ks_s[pl] : scale;
-        float part0 = 0.0f, part1 = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int h = 8 * (i >> 2) + 4 * half + (i & 3);
-            part0 += w_s[2 * wave][h] * fmaxf(acc0[i] * f, 0.0f);
-            part1 += w_s[2 * wave + 1][h] * fmaxf(acc1[i] * f, 0.0f);
-        }
-        float tot0 = add_xor32(part0), tot1 = add_xor32(part1);
-        if (tot0 == 0.0f) tot0 = 0.0f;
-        if (tot1 == 0.0f) tot1 = 0.0f;
-        const int p = p0 + pl;
-        if (half == 0 && p < P) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int r = r0 + j;
-                if (r < Q) {
-                    const bool ok = flag[t] && p < (j ? lim1 : lim0);
-                    scores[(size_t)r * P + p] = ok ? (j ? tot1 : tot0) : -INFINITY;
-                    cand[(size_t)r * P + p] = ok ? 1 : 0;
-                }
-            }
-        }
+    for (int i = 0; i < 16; ++i) {
+        const int h = 8 * (i >> 2) + 4 * half + (i & 3);
+        wr0[i] = w_s[2 * wave][h];
+        wr1[i] = w_s[2 * wave + 1][h];
     }
+
+    // LDS offsets of this lane's key fragments within a 32-pool sub-tile (pool n): the chunk
+    // rotation depends on the pool index only through n, so they are the same for every
+    // sub-tile and buffer.
+    constexpr int kFrags = FP8 ? kSteps / 2 : kSteps;
+    uint32_t koff[kFrags];
+#pragma unroll
+    for (int k = 0; k < kFrags; ++k)
+        koff[k] = (uint32_t)kpos(n, half * (FP8 ? D / 32 : D / 16) + k);
+
+    // The previous tile's scores, stored at the next iteration's start: lane half h writes row
+    // r0 + h (both halves hold both rows' sums).
+    float res[kSub];
+    uint32_t res_ok = 0u;
+    int res_tile = -1;
+    auto store_results = [&]() {
+        const int r = r0 + half;
+        if (res_tile < 0 || r >= Q) return;
+#pragma unroll
+        for (int t = 0; t < kSub; ++t) {
+            const int p = pbase + res_tile * kCB + 32 * t + n;
+            if (p < P) {
+                const bool ok = (res_ok >> t) & 1u;
+                scores[(size_t)r * P + p] = ok ? res[t] : -INFINITY;
+                cand[(size_t)r * P + p] = ok ? 1 : 0;
+            }
+        }
+    };
+
+    for (int it = 0; it < ntiles; ++it) {
+        const uint32_t fl = fl_next;
+        store_results();
+        if (it + 1 < ntiles) {
+            issue_tile(it + 1);
+            fl_next = load_flags(it + 1);
+        }
+        const uint8_t *T = ktile[it & 1];
+#pragma unroll
+        for (int t = 0; t < kSub; ++t) {
+            const int pl = 32 * t + n;  // pool of this lane within the tile
+            const uint8_t *Tt = T + 32 * t * kRowBytes;  // (pl & mask) == (n & mask): koff holds
+            f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+            for (int st = 0; st < kSteps; ++st) {
+                u32x4 kb;
+                if constexpr (FP8) {  // 16 fp8 channels feed two steps
+                    const u32x4 raw = *reinterpret_cast<const u32x4 *>(Tt + koff[st >> 1]);
+                    kb = (st & 1) ? e4m3x8_to_bf16x8(raw.z, raw.w) : e4m3x8_to_bf16x8(raw.x, raw.y);
+                } else {
+                    kb = *reinterpret_cast<const u32x4 *>(Tt + koff[st]);
+                }
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[0][st]), as_bf16x8(kb), acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa[1][st]), as_bf16x8(kb), acc1, 0, 0, 0);
+            }
+            const float f = FP8 ? scale * ks_s[it & 1][pl] : scale;
+            const float tot0 = f * add_xor32(relu_weighted(acc0, wr0, f));
+            const float tot1 = f * add_xor32(relu_weighted(acc1, wr1, f));
+            const float tot = half ? tot1 : tot0;
+            res[t] = tot == 0.0f ? 0.0f : tot;
+        }
+        const int pt = pbase + it * kCB + n;
+        const int lim = half ? lim1 : lim0;
+        res_ok = 0u;
+#pragma unroll
+        for (int t = 0; t < kSub; ++t) res_ok |= (((fl >> t) & 1u) && pt + 32 * t < lim) ? 1u << t : 0u;
+        res_tile = it;
+        wait_vm<0>();     // tile it+1 has landed (and the stores issued above are done)
+        __syncthreads();  // ... for every wave; buffer it&1 is free for tile it+2
+    }
+    store_results();
 }
 
 template <int D, bool FP8>
@@ -374,7 +430,7 @@ hipError_t launch_rowblock_d(int Q, int P, int Hi, int KP, int first_key, float 
                              const uint8_t *pool_valid, float *scores, uint8_t *cand,
                              hipStream_t stream) {
     hipLaunchKernelGGL((index_scores_rowblock_kernel<D, FP8>),
-                       dim3((Q + kRB - 1) / kRB, (P + kCB - 1) / kCB), dim3(kThreads), 0, stream,
+                       dim3((Q + kRB - 1) / kRB, (P + kCB * kTiles - 1) / (kCB * kTiles)), dim3(kThreads), 0, stream,
                        Q, P, Hi, KP, first_key, scale, q, w, row_seq, row_pos, keys, key_scales,
                        pool_valid, scores, cand);
     return hipGetLastError();
