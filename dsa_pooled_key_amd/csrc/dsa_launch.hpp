@@ -56,7 +56,9 @@ struct MlaPlan {
     int groups;      // 32-head groups
     int splits;      // token splits per (row, group)
     int split_len;   // token slots per split (multiple of 32)
-    size_t ws_bytes; // partial results for splits > 1
+    int teams;       // splits per block (1 or 2)
+    int parts;       // blocks per (row, group): ceil(splits / teams)
+    size_t ws_bytes; // partial results for parts > 1
 };
 MlaPlan plan_sparse_mla(int Q, int W, int H);
 hipError_t launch_sparse_mla(const MlaPlan &plan, int Q, int W, int H, int B, float sm_scale,

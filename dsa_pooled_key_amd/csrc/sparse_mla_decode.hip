@@ -77,14 +77,17 @@ __device__ __forceinline__ T lds_load(const uint8_t *base, uint32_t off) {
     return *reinterpret_cast<const T *>(base + off);
 }
 
-// Block = 4 waves. Wave v scores tile rows 16*(v>>1).. x heads 16*(v&1).. and accumulates O
-// for channels 128v..128v+127 of all 32 heads of group g.
+// Team = 4 waves working one token split. Wave v scores tile rows 16*(v>>1).. x heads
+// 16*(v&1).. and accumulates O for channels 128v..128v+127 of all 32 heads of group g.
+// A block holds TEAMS teams on consecutive splits of the same row and head group: they share
+// the staged query rows and every barrier, and merge their (max, sum, O) in LDS at the end,
+// so the block leaves one partial (or, covering the whole row, the output itself).
 //
 // Query channels are permuted inside each MFMA step (the contraction order is free as long
 // as both operands agree): step s, lane group k (= lane>>4) covers channels
 // 64*(s>>1) + 16k + 8*(s&1) .. +7, so one 16-byte read of an fp8 row feeds two steps.
-template <bool FP8, bool PAGED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void sparse_mla_kernel(
+template <bool FP8, bool PAGED, int TEAMS>
+__global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_eu(2))) void sparse_mla_kernel(
     int W, int H, int B, int splits, int split_len, float sm_scale,
     const uint16_t *__restrict__ q_abs, const int32_t *__restrict__ token_ids,
     const int32_t *__restrict__ row_seq, const void *__restrict__ kv,
@@ -95,25 +98,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     constexpr int NS = G_::kStages;
     constexpr int RB = G_::kRowBytes;
 
-    __shared__ __attribute__((aligned(16))) uint8_t ring[NS * G_::kTileBytes];
-    __shared__ __attribute__((aligned(16))) uint16_t pl[32 * kPStride];
-    __shared__ __attribute__((aligned(16))) int rows_s[kMaxSplit];
+    static_assert(TEAMS == 1 || TEAMS == 2, "one or two teams per block");
+    // One set per team.
+    __shared__ __attribute__((aligned(16))) uint8_t ring_all[TEAMS][NS * G_::kTileBytes];
+    __shared__ __attribute__((aligned(16))) uint16_t pl_all[TEAMS][32 * kPStride];
+    __shared__ __attribute__((aligned(16))) int rows_all[TEAMS][kMaxSplit];
     // fp8 scales of each resident tile: wave w's 8 rows at [stage][w][0..7] (64 per wave land).
-    __shared__ __attribute__((aligned(16))) float sc_ring[FP8 ? NS : 1][4][kWave];
-    __shared__ float red[4][16];
-    __shared__ float alpha_s[32];
-    __shared__ float msum_s[32];
-    __shared__ float lsum_s[32];
-    __shared__ int last_w[4];
-    __shared__ int rescale_s[2];
+    __shared__ __attribute__((aligned(16))) float sc_all[TEAMS][FP8 ? NS : 1][4][kWave];
+    __shared__ float red_all[TEAMS][4][16];
+    __shared__ float alpha_all[TEAMS][32];
+    __shared__ float msum_all[TEAMS][32];
+    __shared__ float lsum_all[TEAMS][32];
+    __shared__ int last_all[TEAMS][4];
+    __shared__ int rescale_all[TEAMS][2];
+    __shared__ __attribute__((aligned(16))) float mf_s[TEAMS][32];  // per-head merge factors
 
     const int r = blockIdx.x;
-    const int split = blockIdx.y;
+    const int tm = threadIdx.x / kThreads;  // team
+    const int split = blockIdx.y * TEAMS + tm;
     const int g = blockIdx.z;
     const int G = gridDim.z;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x % kThreads;  // thread within the team
     const int lane = tid & (kWave - 1);
-    const int v = tid / kWave;  // wave 0..3
+    const int v = tid / kWave;  // wave 0..3 of the team
+    uint8_t *const ring = ring_all[tm];
+    uint16_t *const pl = pl_all[tm];
+    int *const rows_s = rows_all[tm];
+    float(*const sc_ring)[4][kWave] = sc_all[tm];
+    float(*const red)[16] = red_all[tm];
+    float *const alpha_s = alpha_all[tm];
+    float *const msum_s = msum_all[tm];
+    float *const lsum_s = lsum_all[tm];
+    int *const last_w = last_all[tm];
+    int *const rescale_s = rescale_all[tm];
     const int lg = lane >> 4;   // 16-lane group
     const int b = row_seq[r];
     const bool row_ok = b >= 0 && b < B;
@@ -122,14 +139,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const uint8_t *kvb = static_cast<const uint8_t *>(kv);
 
     // The block's 32 query rows (1 KiB each) are staged once through LDS, in the upper half of
-    // the ring, which no tile uses before every wave has taken its fragment: wave v fetches
-    // heads 8v..8v+7, chunk c of head row h at position c ^ swz<false>(h).
-    uint8_t *const qlds = ring + 32768;
+    // team 0's ring, which no tile uses before every wave of the block has taken its fragment:
+    // wave w of the block fetches 8/TEAMS heads from (8/TEAMS)w on, chunk c of head row h at
+    // position c ^ swz<false>(h).
+    uint8_t *const qlds = ring_all[0] + 32768;
     const int qk_head_local = 16 * (v & 1) + (lane & 15);
     const int qk_head = g * 32 + qk_head_local;
+    constexpr int kQHeads = 8 / TEAMS;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int hl = 8 * v + k;
+    for (int k = 0; k < kQHeads; ++k) {
+        const int hl = kQHeads * (int)(threadIdx.x / kWave) + k;
         if (g * 32 + hl < H)
             dma16(reinterpret_cast<const uint8_t *>(q_abs + ((size_t)r * H + g * 32 + hl) * kC) +
                       16 * (lane ^ swz<false>(hl)),
@@ -217,6 +236,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __syncthreads();
     const int last = max(max(last_w[0], last_w[1]), max(last_w[2], last_w[3]));
     const int n_tiles = (last + kTile) / kTile;  // through the last slot with a token
+    // The teams step through n_iter tiles together, since the barriers are the block's; a team
+    // past its own last tile keeps only the barriers.
+    int n_iter = n_tiles;
+    if constexpr (TEAMS == 2) {
+        const int *lo = last_all[tm ^ 1];
+        n_iter = max(n_iter, (max(max(lo[0], lo[1]), max(lo[2], lo[3])) + kTile) / kTile);
+    }
 
     // Query fragment for S^T = K Q^T (B operand): head column lane&15 of this wave's 16; step st,
     // lane group lg holds channels 64(st>>1) + 16lg + 8(st&1) .. +7 (chunk 8(st>>1) + 2lg + (st&1)).
@@ -403,14 +429,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             else wait_vm<0>();
             lds_barrier();  // C
         };
-        if (n_tiles > 0) {
+        if (n_iter > 0) {
             float x[4], sc[4];
-            scores(0, x, sc);
+            if (n_tiles > 0) scores(0, x, sc);
             lds_barrier();  // B; every wave holds its query fragment, so stage 2 is free
-            if (2 < n_tiles) issue(2);
-            softmax(0, x, sc);
-            if (2 < n_tiles) wait_vm<G_::kLoadsT>();
-            else wait_vm<0>();
+            if (n_tiles > 0) {
+                if (2 < n_tiles) issue(2);
+                softmax(0, x, sc);
+                if (2 < n_tiles) wait_vm<G_::kLoadsT>();
+                else wait_vm<0>();
+            }
             lds_barrier();  // C
         }
         // Iteration t: every LDS operand of the refill, of the products of tile t-1 and of the
@@ -462,26 +490,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             }
             score_epilogue(sa, sb, rw, sv, x, sc);
         };
-        for (int t = 1; t < n_tiles; ++t) {
+        for (int t = 1; t < n_iter; ++t) {
             float x[4], sc[4];
-            step(t, x, sc);
-            finish_tile(t, x, sc);
+            if (t < n_tiles) {
+                step(t, x, sc);
+                finish_tile(t, x, sc);
+            } else {
+                if (t == n_tiles) products(t - 1);  // the team's last tile
+                lds_barrier();  // B
+                lds_barrier();  // C
+            }
         }
-        if (n_tiles > 0) products(n_tiles - 1);
+        if (n_tiles > 0 && n_tiles == n_iter) products(n_tiles - 1);
     } else {
         // bf16: one tile in flight (two 32 KiB stages); barrier A opens each tile once it is
         // resident and the stage of tile t-1 is free for tile t+1 (for t = 0: the query rows
         // in stage 1 have been read by every wave).
-        for (int t = 0; t < n_tiles; ++t) {
+        for (int t = 0; t < n_iter; ++t) {
             float x[4], sc[4];
+            const bool act = t < n_tiles;
             wait_vm<0>();
             lds_barrier();  // A
-            if (t + 1 < n_tiles) issue(t + 1);
-            scores(t, x, sc);
+            if (act) {
+                if (t + 1 < n_tiles) issue(t + 1);
+                scores(t, x, sc);
+            }
             lds_barrier();  // B
-            softmax(t, x, sc);
+            if (act) softmax(t, x, sc);
             lds_barrier();  // C
-            products(t);
+            if (act) products(t);
         }
     }
 
@@ -497,7 +534,53 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     __syncthreads();
 
-    if (splits == 1) {
+    if constexpr (TEAMS == 2) {
+        // Team 1 hands its accumulator to team 0 through its own ring (idle now: its tiles have
+        // landed and been used), f32 in accumulator order. Per head the merged maximum M, the
+        // factors e^(m - M) (0 for a team without tokens) and the merged sum are formed once.
+        f32x4 *xch = reinterpret_cast<f32x4 *>(ring_all[1]);
+        if (tm == 1) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4)
+                    xch[((v * 4 + nt) * 4 + i4) * kWave + lane] =
+                        f32x4{acc[nt][4 * i4], acc[nt][4 * i4 + 1], acc[nt][4 * i4 + 2], acc[nt][4 * i4 + 3]};
+        }
+        if (threadIdx.x < 32) {
+            const int h = threadIdx.x;
+            const float ma = msum_all[0][h], mb = msum_all[1][h];
+            const float la = lsum_all[0][h], lb = lsum_all[1][h];
+            float M = -INFINITY;
+            if (la > 0.0f) M = ma;
+            if (lb > 0.0f) M = fmaxf(M, mb);
+            const float fa = la > 0.0f ? fast_exp(ma - M) : 0.0f;
+            const float fb = lb > 0.0f ? fast_exp(mb - M) : 0.0f;
+            mf_s[0][h] = fa;
+            mf_s[1][h] = fb;
+            msum_all[0][h] = M;
+            lsum_all[0][h] = la * fa + lb * fb;
+        }
+        __syncthreads();
+        if (tm == 1) return;
+        const int m0 = 4 * (lane >> 5);  // heads m0 + 8j .. +3 for element group j
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 fa = *reinterpret_cast<const f32x4 *>(&mf_s[0][8 * i4 + m0]);
+            const f32x4 fb = *reinterpret_cast<const f32x4 *>(&mf_s[1][8 * i4 + m0]);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const f32x4 o = xch[((v * 4 + nt) * 4 + i4) * kWave + lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[nt][4 * i4 + e] = acc[nt][4 * i4 + e] * fa[e] + o[e] * fb[e];
+            }
+        }
+    }
+
+    // The block's result: out and lse when it covers the whole row, else partial blockIdx.y.
+    const int parts = gridDim.y;
+    if (parts == 1) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             const int ch = 128 * v + 32 * nt + (lane & 31);
@@ -514,12 +597,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             lse[(size_t)r * H + g * 32 + tid] = L > 0.0f ? msum_s[tid] + logf(L) : -INFINITY;
         }
     } else {
-        uint8_t *part = reinterpret_cast<uint8_t *>(ws) + (((size_t)r * G + g) * splits + split) * kPartBytes;
+        uint8_t *part = reinterpret_cast<uint8_t *>(ws) + (((size_t)r * G + g) * parts + blockIdx.y) * kPartBytes;
         if (tid < 32) {
             reinterpret_cast<float *>(part)[tid] = msum_s[tid];
             reinterpret_cast<float *>(part)[32 + tid] = lsum_s[tid];
         }
-        if (n_tiles > 0) {  // a split without tokens leaves O unwritten; its sum is 0
+        if (n_iter > 0) {  // a block without tokens leaves O unwritten; its sum is 0
             u32x4 *po = reinterpret_cast<u32x4 *>(part + kPartHeader);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
@@ -641,23 +724,30 @@ hipError_t launch_v(const MlaPlan &plan, int Q, int W, int H, int B, float sm_sc
                     const void *kv, const float *kv_scales, int64_t kv_rows, int S,
                     const int32_t *block_table, int max_blocks, int block_size, float *out,
                     float *lse, void *ws, hipStream_t stream) {
-    hipLaunchKernelGGL((sparse_mla_kernel<FP8, PAGED>), dim3(Q, plan.splits, plan.groups),
-                       dim3(kThreads), 0, stream, W, H, B, plan.splits, plan.split_len, sm_scale,
-                       q_abs, token_ids, row_seq, kv, kv_scales, (long long)kv_rows, S,
-                       block_table, max_blocks, block_size, out, lse,
-                       static_cast<float *>(ws));
+    const dim3 grid(Q, plan.parts, plan.groups);
+    if (plan.teams == 2)
+        hipLaunchKernelGGL((sparse_mla_kernel<FP8, PAGED, 2>), grid, dim3(2 * kThreads), 0, stream, W, H, B,
+                           plan.splits, plan.split_len, sm_scale, q_abs, token_ids, row_seq, kv, kv_scales,
+                           (long long)kv_rows, S, block_table, max_blocks, block_size, out, lse,
+                           static_cast<float *>(ws));
+    else
+        hipLaunchKernelGGL((sparse_mla_kernel<FP8, PAGED, 1>), grid, dim3(kThreads), 0, stream, W, H, B,
+                           plan.splits, plan.split_len, sm_scale, q_abs, token_ids, row_seq, kv, kv_scales,
+                           (long long)kv_rows, S, block_table, max_blocks, block_size, out, lse,
+                           static_cast<float *>(ws));
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || plan.splits == 1) return e;
-    hipLaunchKernelGGL(mla_combine_kernel, dim3(Q, plan.groups, 16), dim3(128), 0, stream, H, plan.splits,
+    if (e != hipSuccess || plan.parts == 1) return e;
+    hipLaunchKernelGGL(mla_combine_kernel, dim3(Q, plan.groups, 16), dim3(128), 0, stream, H, plan.parts,
                        static_cast<const uint8_t *>(ws), out, lse);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Split the token slots so that about 512 blocks (two 4-wave blocks per compute unit) run,
+// Split the token slots so that about 512 teams (two 4-wave teams per compute unit) run,
 // with at least 64 slots per split, at most kMaxSplit slots per split and at most
-// kMaxSplits splits; a row that already gives enough blocks is not split.
+// kMaxSplits splits; a row that already gives enough teams is not split. Where the splits
+// still give two teams per compute unit, pairs of splits share a block (one partial per pair).
 MlaPlan plan_sparse_mla(int Q, int W, int H) {
     MlaPlan p;
     p.groups = (H + 31) / 32;
@@ -677,7 +767,9 @@ MlaPlan plan_sparse_mla(int Q, int W, int H) {
         p.splits = (int)((W + per - 1) / per);
     }
     p.split_len = (int)per;
-    p.ws_bytes = p.splits > 1 ? (size_t)Q * p.groups * p.splits * kPartBytes : 0;
+    p.teams = p.splits > 1 && (long long)Q * p.groups * p.splits >= 512 ? 2 : 1;
+    p.parts = (p.splits + p.teams - 1) / p.teams;
+    p.ws_bytes = p.parts > 1 ? (size_t)Q * p.groups * p.parts * kPartBytes : 0;
     return p;
 }
 

@@ -328,6 +328,38 @@ def test_sparse_mla_decode(name):
     _check_mla(out.cpu().numpy()[rows], lse.cpu().numpy()[rows], ro, rl, wl.kv_fp8)
 
 
+@pytest.mark.parametrize("name,n_rows", [("ragged_bf16", 66), ("ragged_fp8", 181)])
+def test_sparse_mla_paired_splits(name, n_rows):
+    """Enough rows that two splits of a row share one block and merge in LDS (bf16: two head
+    groups, 4 splits; fp8 paged: 3 splits, so the last block's second split is empty). Rows 0-3
+    are emptied so that either split of a pair, both or neither hold tokens."""
+    di, x, _, _ = case(name)
+    wl = di.wl
+    cfg = config_for(wl)
+    rng = np.random.default_rng(11)
+    k = (n_rows + wl.Q - 1) // wl.Q
+    q = np.tile(di.q_abs, (k, 1, 1))[:n_rows]
+    rs = np.tile(di.row_seq, k)[:n_rows].astype(np.int32)
+    tok = np.tile(synth.draw_token_ids(di), (k, 1))[:n_rows]
+    tok = np.take_along_axis(tok, rng.permuted(np.tile(np.arange(tok.shape[1]), (n_rows, 1)), axis=1), 1)
+    W = tok.shape[1]
+    tok[0] = -1                # no tokens at all
+    tok[1, 64:] = -1           # only the first split
+    tok[2, :64] = -1           # the second split only
+    tok[2, 128:] = -1
+    tok[3, :128] = -1          # only the splits from slot 128 on
+    tok = np.ascontiguousarray(tok)
+    assert W > 128
+    qd = torch.from_numpy(np.ascontiguousarray(q).view(np.int16)).cuda().view(torch.bfloat16)
+    out, lse = dsa.sparse_mla_decode(cfg, qd, _dev(tok), _dev(rs), x.kv, B=wl.B,
+                                     sm_scale=di.sm_scale, S=wl.S, kv_scales=x.kv_scales,
+                                     block_table=x.block_table)
+    ro, rl = oracle.sparse_mla(q, tok, rs, di.kv, sm_scale=di.sm_scale, S=wl.S,
+                               kv_scales=di.kv_scales, block_table=di.block_table)
+    _check_mla(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, wl.kv_fp8)
+    assert np.all(np.isneginf(lse.cpu().numpy()[0]))
+
+
 def test_sparse_mla_repeatable_paging_invariant_and_masks_bad_ids():
     di, x, _, _ = case("ragged_bf16")
     wl = di.wl
