@@ -746,8 +746,11 @@ hipError_t launch_v(const MlaPlan &plan, int Q, int W, int H, int B, float sm_sc
 
 // Split the token slots so that about 512 teams (two 4-wave teams per compute unit) run,
 // with at least 64 slots per split, at most kMaxSplit slots per split and at most
-// kMaxSplits splits; a row that already gives enough teams is not split. Where the splits
-// still give two teams per compute unit, pairs of splits share a block (one partial per pair).
+// kMaxSplits splits; a row that already gives enough teams is not split. Where the teams fill
+// one or two waves of resident blocks (512 to 1024 of them), pairs of splits share a block
+// (one partial per pair). Larger grids keep one team per block: two blocks on a compute unit
+// then drift apart in phase, so one's prologue overlaps the other's streaming, which paired
+// teams in lockstep would lose.
 MlaPlan plan_sparse_mla(int Q, int W, int H) {
     MlaPlan p;
     p.groups = (H + 31) / 32;
@@ -767,7 +770,8 @@ MlaPlan plan_sparse_mla(int Q, int W, int H) {
         p.splits = (int)((W + per - 1) / per);
     }
     p.split_len = (int)per;
-    p.teams = p.splits > 1 && (long long)Q * p.groups * p.splits >= 512 ? 2 : 1;
+    const long long teams = (long long)Q * p.groups * p.splits;
+    p.teams = p.splits > 1 && teams >= 512 && teams <= 1024 ? 2 : 1;
     p.parts = (p.splits + p.teams - 1) / p.teams;
     p.ws_bytes = p.parts > 1 ? (size_t)Q * p.groups * p.parts * kPartBytes : 0;
     return p;
