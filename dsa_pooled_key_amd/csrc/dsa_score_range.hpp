@@ -85,14 +85,26 @@ __device__ __forceinline__ void score_range(
     const bool row_ok = b >= 0 && b < B;
     const long long lim = row_pool_limit(b, pos, B, P, KP, first_key);
 
-    // Round trip 2: the validity flags of this lane's slots; round trip 3: their keys.
+    // Round trip 2: the validity flags of this lane's slots; round trip 3: their keys. The
+    // flags sit under one branch that is uniform over the wave (a lane past the row's limit
+    // reads the last flag in range and drops it), so they are requested together: under a
+    // branch per tile the compiler waits for each flag before requesting the next.
     int slot[TPW];
     bool ok[TPW];
+    uint32_t flag[TPW];
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         slot[t] = slot0 + (t * kWaves + wave) * 32 + n;
-        ok[t] = slot[t] < lim && pool_valid[(size_t)b * P + slot[t]] != 0;
+        flag[t] = 0u;
     }
+    if (slot0 + wave_u * 32 < lim) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+            flag[t] = pool_valid[(size_t)b * P + (slot[t] < lim ? slot[t] : (int)lim - 1)];
+    }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) ok[t] = slot[t] < lim && flag[t] != 0u;
     u32x4 raw[TPW][FP8 ? kHalf / 16 : kSteps];
     float ksc[TPW];
     bool any[TPW];
