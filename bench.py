@@ -272,13 +272,8 @@ def run_gpu(args):
 
     # Per-stage durations: each stage alone, same replicas, same graph replay.
     stage_fns = {
-        "compact_index_scores": lambda s: dsa.compact_index_scores(
-            s.cfg, s.x.q, s.x.w, s.x.row_seq, s.x.row_pos, s.x.keys, s.x.pool_valid,
-            first_key=wl.first_key, scale=s.scale, key_scales=s.x.key_scales, scores=s.scores,
-            cand=s.cand),
-        "topk_expand": lambda s: dsa.topk_expand(
-            s.cfg, s.scores, s.cand, s.x.row_seq, s.x.row_pos, s.x.valid, S=wl.S,
-            first_key=wl.first_key, sel=s.sel, token_ids=s.token_ids),
+        "compact_index_scores": lambda s: s.score(),
+        "topk_expand": lambda s: s.topk(),
         "sparse_mla_decode": lambda s: s.attend(),
     }
     stage_us = {}

@@ -36,6 +36,9 @@ struct ExpandArgs {
 
 
 constexpr int kMaxMembers = kWave;  // cutoff bins up to this size are ranked by one wave
+// Selections up to this width are staged in LDS and written (with their token ids) by
+// consecutive threads, one pool each; wider ones are written by the selecting threads.
+constexpr int kStageSel = 2048;
 
 // LDS of one row's selection.
 struct Smem {
@@ -44,6 +47,7 @@ struct Smem {
     uint32_t hist[256];
     __attribute__((aligned(16))) uint32_t bins[kBins];
     uint32_t mem[kMaxMembers];
+    int sel_s[kStageSel];
     int n_mem;
     uint32_t pick[3];
 };
@@ -307,9 +311,8 @@ __device__ __forceinline__ void select_row(int r, int P, int Kw, uint32_t (&key)
         smask |= emask & (0ull - emask);
         emask &= emask - 1ull;
     }
-    while (smask != 0u && o < Kw) {
-        const int p = base + __builtin_ctzll(smask);
-        smask &= smask - 1ull;
+    // Selected pool p at output position o: its id and, fused, its KP token ids.
+    auto write_pool = [&](int o, int p) {
         orow[o] = p;
         if constexpr (EXPAND) {
             const int t0 = ex.first_key + p * ex.KP;
@@ -321,9 +324,28 @@ __device__ __forceinline__ void select_row(int r, int P, int Kw, uint32_t (&key)
                 for (int t = 0; t < ex.KP; ++t) dst[t] = t0 + t;
             }
         }
-        ++o;
+    };
+    if (Kw <= kStageSel) {
+        // The ids go to LDS at their positions; after one barrier thread j writes position j,
+        // so a row whose selection sits in few threads (a context of few pools) still spreads
+        // its stores over the block, and ids and token ids go out in coalesced runs.
+        while (smask != 0u && o < Kw) {
+            sm.sel_s[o++] = base + __builtin_ctzll(smask);
+            smask &= smask - 1ull;
+        }
+        __syncthreads();
+        for (int j = tid; j < Kw; j += kThreads) {
+            if (j < take) write_pool(j, sm.sel_s[j]);
+            else orow[j] = -1;
+        }
+    } else {
+        while (smask != 0u && o < Kw) {
+            write_pool(o, base + __builtin_ctzll(smask));
+            smask &= smask - 1ull;
+            ++o;
+        }
+        for (int i = take + tid; i < Kw; i += kThreads) orow[i] = -1;
     }
-    for (int i = take + tid; i < Kw; i += kThreads) orow[i] = -1;
     if constexpr (EXPAND) {
         // The remaining token slots (as expand_selection): -1 up to topk, then the tail tokens
         // after the last whole pool up to row_pos, each only if valid.

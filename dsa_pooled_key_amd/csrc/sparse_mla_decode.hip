@@ -602,7 +602,7 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
             reinterpret_cast<float *>(part)[tid] = msum_s[tid];
             reinterpret_cast<float *>(part)[32 + tid] = lsum_s[tid];
         }
-        if (n_iter > 0) {  // a block without tokens leaves O unwritten; its sum is 0
+        {  // a block without tokens writes its zero O too (sum 0), so the merge needs no test
             u32x4 *po = reinterpret_cast<u32x4 *>(part + kPartHeader);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
@@ -620,8 +620,7 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
 // Merge the split partials of one (row, head group): block z = 4v + nt covers channels
 // 128v + 32nt .. +31 of all 32 heads. Per head the splits' (max m_s, sum l_s) give
 // M = max m_s, L = sum l_s e^(m_s - M) and the weights e^(m_s - M) / L; out = sum_s weight_s O_s,
-// lse = M + log L. Splits without tokens (l_s = 0) take no part; their O, never written, is
-// read but not used.
+// lse = M + log L. Splits without tokens (l_s = 0) get weight 0; their O is zero.
 __global__ __launch_bounds__(128) void mla_combine_kernel(int H, int splits,
                                                           const uint8_t *__restrict__ ws,
                                                           float *__restrict__ out,
@@ -695,7 +694,7 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(int H, int splits,
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const float x = (c & 1) ? bf16_hi(u[c >> 1]) : bf16_lo(u[c >> 1]);
-            o[c] += w[c] != 0.0f ? x * w[c] : 0.0f;
+            o[c] = fmaf(x, w[c], o[c]);
         }
     };
 #pragma unroll

@@ -85,6 +85,10 @@ class DecodeStep:
         self.ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
 
     def select(self):
+        self.score()
+        self.topk()
+
+    def score(self):
         x, wl = self.x, self.wl
         if self.fused:
             dsa.compact_index_scores(self.cfg, x.q, x.w, x.row_seq, x.row_pos, x.keys,
@@ -95,6 +99,9 @@ class DecodeStep:
             dsa.index_scores(self.cfg, x.q, x.w, x.row_seq, x.row_pos, x.keys, self.ids,
                              self.n_valid, first_key=wl.first_key, scale=self.scale,
                              key_scales=x.key_scales, scores=self.scores, cand=self.cand)
+
+    def topk(self):
+        x, wl = self.x, self.wl
         if self.fused:
             dsa.topk_expand(self.cfg, self.scores, self.cand, x.row_seq, x.row_pos, x.valid,
                             S=wl.S, first_key=wl.first_key, sel=self.sel, token_ids=self.token_ids)
