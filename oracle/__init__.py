@@ -68,6 +68,10 @@ def lib():
         L.orc_sparse_mla.argtypes = [_I, _I, _I, _I, _D, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I,
                                      _P, _P]
         L.orc_sparse_mla.restype = None
+        L.orc_e4m3_from_float.argtypes = [ctypes.c_float]
+        L.orc_e4m3_from_float.restype = ctypes.c_uint8
+        L.orc_quantize_rows.argtypes = [_L, _I, _P, _P, _P]
+        L.orc_quantize_rows.restype = None
         L.orc_absorb_q.argtypes = [_I, _I, _I, _I, _I, _I, _P, _L, _P, _L, _P, ctypes.c_char_p, _I]
         L.orc_absorb_q.restype = _I
         L.orc_absorb_o.argtypes = [_I, _I, _I, _I, _I, _I, _P, _L, _P, _L, _P, ctypes.c_char_p, _I]
@@ -137,6 +141,33 @@ def kpool_compress(k, gate, ape, valid, kpool: int, first_key: int):
     lib().orc_kpool_compress(B, S, D, kpool, first_key, _ptr(k), _ptr(gate), _ptr(ape),
                              _ptr(valid), _ptr(pk), _ptr(pv))
     return pk, pv
+
+
+def e4m3_from_float(x: float) -> int:
+    """OCP e4m3 code of a binary32 value: nearest, ties to even, saturating at +-448."""
+    return int(lib().orc_e4m3_from_float(float(x)))
+
+
+def quantize_rows(x):
+    """Per-row fp8: x [..., n] float32 values -> (codes uint8 [..., n], scales f32 [...]) with
+    s = amax/448 (1 for an all-zero row) and codes e4m3(x / s), both divisions in f32."""
+    x = np.ascontiguousarray(x, np.float32)
+    n = x.shape[-1]
+    rows = x.size // n if n else 0
+    codes = np.zeros(x.shape, np.uint8)
+    scales = np.zeros(x.shape[:-1], np.float32)
+    if rows:
+        lib().orc_quantize_rows(rows, n, _ptr(x), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def kpool_compress_fp8(k, gate, ape, valid, kpool: int, first_key: int):
+    """Pooled keys stored as fp8: the bf16 pooled key of kpool_compress, quantized per pool
+    row by quantize_rows. Returns (codes [B,P,D] uint8, scales [B,P] f32, pool_valid [B,P])."""
+    pk, pv = kpool_compress(k, gate, ape, valid, kpool, first_key)
+    vals = (pk.astype(np.uint32) << 16).view(np.float32)
+    codes, scales = quantize_rows(vals)
+    return codes, scales, pv
 
 
 def compact_pools(pool_valid):

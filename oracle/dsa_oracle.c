@@ -118,6 +118,50 @@ int orc_validate(long index_kpool, long index_topk, long kv_lora_rank, long loca
     return 0;
 }
 
+/* ---------------------------------------------------------------- fp8 writers */
+
+/* binary32 -> OCP E4M3 ("FN") code: the representable value nearest to x, ties to the code
+ * with an even mantissa, magnitudes beyond the largest normal (448) saturating to it; the
+ * sign is kept (so a negative value that rounds to zero gives 0x80). Found by binary search
+ * over the 127 non-negative finite values of e4m3_value, compared in double. */
+static uint8_t e4m3_from_float(float x) {
+    double a = fabs((double)x);
+    uint8_t sign = signbit(x) ? 0x80u : 0x00u;
+    int lo = 0, hi = 0x7e; /* codes 0 .. 0x7e are the non-negative finite values, ascending */
+    if (a >= e4m3_value(0x7e)) return (uint8_t)(sign | 0x7e);
+    while (hi - lo > 1) { /* invariant: value(lo) <= a < value(hi) */
+        int mid = (lo + hi) / 2;
+        if (e4m3_value((uint8_t)mid) <= a) lo = mid;
+        else hi = mid;
+    }
+    double dl = a - e4m3_value((uint8_t)lo), dh = e4m3_value((uint8_t)hi) - a;
+    int code = dl < dh ? lo : (dh < dl ? hi : ((lo & 1) ? hi : lo));
+    return (uint8_t)(sign | code);
+}
+
+uint8_t orc_e4m3_from_float(float x) { return e4m3_from_float(x); }
+
+/* Per-row fp8 quantizer (the reading of the stored fp8 format: per row scale
+ * s = amax / 448 with amax the largest |x| of the row, s = 1 for an all-zero row; each value
+ * stored as e4m3(x / s), so that the row is code * s). s and x / s are single-precision
+ * divisions, as the stored scale is f32. Layouts: x [rows, n] f32 values; codes [rows, n];
+ * scales [rows]. */
+void orc_quantize_rows(long rows, int n, const float *x, uint8_t *codes, float *scales) {
+    for (long r = 0; r < rows; ++r) {
+        float amax = 0.0f;
+        for (int i = 0; i < n; ++i) {
+            float a = fabsf(x[r * n + i]);
+            if (a > amax) amax = a;
+        }
+        volatile float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+        scales[r] = s;
+        for (int i = 0; i < n; ++i) {
+            volatile float q = x[r * n + i] / s;
+            codes[r * n + i] = e4m3_from_float(q);
+        }
+    }
+}
+
 /* ---------------------------------------------------------------- step 1: kpool_compress */
 
 /* mod.rs, "Shape of the pipeline" (k, gate, valid, ape -> pool keys / indices / valid) and

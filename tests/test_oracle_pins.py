@@ -669,3 +669,95 @@ def test_tiny_chain_selects_the_pools_a_brute_force_ranking_picks():
     assert np.allclose(sc[0, :255], ref[:255], rtol=1e-6, atol=1e-6)
     sel = oracle.topk_pools(sc, cd, wl.kw)
     assert list(sel[0]) == _rank_select(sc[0], cd[0], wl.kw)
+
+
+# ------------------------------------------------------------------ fp8 writers
+
+def test_e4m3_encoder_round_trips_every_code_and_the_ocp_table():
+    """Every finite code decodes (by the OCP definition, pinned above) to a value that encodes
+    back to the same code; the printed table values encode to their printed codes."""
+    for c in range(256):
+        v = oracle.e4m3_value(c)
+        if np.isnan(v):
+            continue
+        assert oracle.e4m3_from_float(np.float32(v)) == c, hex(c)
+    for code, value in _rows("e4m3_ocp.txt"):
+        if value != "nan":
+            assert oracle.e4m3_from_float(float(value)) == int(code, 16)
+
+
+def test_e4m3_encoder_ties_to_even_and_saturates():
+    """Midpoints between neighbouring values (exact in binary32) go to the even mantissa, a
+    hair off a midpoint goes to the nearer value, and magnitudes past 448 saturate."""
+    for c in range(0, 0x7e):
+        lo, hi = oracle.e4m3_value(c), oracle.e4m3_value(c + 1)
+        mid = (lo + hi) / 2
+        assert np.float32(mid) == mid
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.e4m3_from_float(mid) == even
+        assert oracle.e4m3_from_float(-mid) == 0x80 | even
+        assert oracle.e4m3_from_float(np.nextafter(np.float32(mid), np.float32(0))) == c
+        assert oracle.e4m3_from_float(np.nextafter(np.float32(mid), np.float32(1e9))) == c + 1
+    for big in (448.0, 449.0, 464.0, 480.0, 1e6, 3.0e38):
+        assert oracle.e4m3_from_float(big) == 0x7e and oracle.e4m3_from_float(-big) == 0xfe
+    assert oracle.e4m3_from_float(0.0) == 0x00 and oracle.e4m3_from_float(-0.0) == 0x80
+
+
+def test_quantize_rows_scale_amax_and_error_bound():
+    """s = amax/448 and the largest element maps to +-448; a zero row has scale 1; scaling a
+    row by a power of two scales s and keeps the codes; every dequantized value lies within
+    half a step of the e4m3 grid around x/s (relative 2^-4 for normals, 2^-10 absolute below
+    2^-6), times s."""
+    rng = np.random.default_rng(40)
+    x = (rng.standard_normal((50, 96)) * np.exp(rng.uniform(-8, 8, (50, 1)))).astype(np.float32)
+    x[3] = 0.0
+    x[4, :] = 0.0
+    x[4, 7] = -3.5
+    codes, s = oracle.quantize_rows(x)
+    amax = np.abs(x).max(axis=1)
+    assert s[3] == 1.0 and np.all(codes[3] == 0)
+    for r in range(50):
+        if amax[r] == 0:
+            continue
+        assert s[r] == np.float32(amax[r] / np.float32(448.0))
+        j = int(np.argmax(np.abs(x[r])))
+        assert codes[r, j] == (0xfe if x[r, j] < 0 else 0x7e)
+        deq = np.array([oracle.e4m3_value(int(c)) for c in codes[r]]) * np.float64(s[r])
+        xs = x[r].astype(np.float64) / np.float64(s[r])
+        bound = np.where(np.abs(xs) >= 2.0 ** -6, np.abs(xs) * 2.0 ** -4, 2.0 ** -10) * s[r]
+        assert np.all(np.abs(deq - x[r]) <= bound * (1 + 1e-6))
+    c2, s2 = oracle.quantize_rows(x * np.float32(8.0))
+    assert np.array_equal(c2, codes) and np.array_equal(s2[amax > 0], s[amax > 0] * 8)
+
+
+def test_kpool_compress_fp8_is_the_bf16_pooled_key_quantized():
+    """The fp8 pooled key decodes to the bf16 pooled key within the quantizer's bound, and on
+    one-hot pooling of keys that are e4m3 values times a power of two it is exact."""
+    rng = np.random.default_rng(41)
+    B, S, D, KP = 2, 37, 32, 4
+    k = synth.bf16_bits(rng.standard_normal((B, S, D)).astype(np.float32))
+    gate = synth.bf16_bits(rng.standard_normal((B, S, D)).astype(np.float32))
+    ape = rng.standard_normal((KP, D)).astype(np.float32)
+    valid = (rng.random((B, S)) > 0.1).astype(np.uint8)
+    codes, sc, pv = oracle.kpool_compress_fp8(k, gate, ape, valid, KP, 1)
+    pk, pv2 = oracle.kpool_compress(k, gate, ape, valid, KP, 1)
+    assert np.array_equal(pv, pv2)
+    vals = synth.bf16_to_f32(pk).astype(np.float64)
+    deq = np.vectorize(oracle.e4m3_value)(codes) * sc[..., None].astype(np.float64)
+    assert np.all(np.abs(deq - vals) <= np.abs(vals) * 2.0 ** -4 + sc[..., None] * 2.0 ** -10 + 1e-30)
+    # one-hot: slot 2 wins (ape +64 against -64), keys m/8 with |m| <= 8: pooled key = that
+    # slot's key, amax a power of two times (1..8)/8, codes exact
+    ape1 = np.full((KP, D), -64.0, np.float32)
+    ape1[2] = 64.0
+    kk = synth.bf16_bits((rng.integers(-8, 9, (B, S, D)) / 8.0).astype(np.float32))
+    kk[:, :, 0] = synth.bf16_bits(np.float32(1.0))  # amax = 1 in every pool
+    z = np.zeros_like(kk)
+    codes, sc, _ = oracle.kpool_compress_fp8(kk, z, ape1, valid, KP, 0)
+    P = codes.shape[1]
+    assert np.all(sc == np.float32(1.0 / 448.0))
+    src = synth.bf16_to_f32(kk[:, 2:2 + P * KP:KP])
+    want = np.vectorize(lambda v: oracle.e4m3_from_float(np.float32(v) / np.float32(1.0 / 448.0)))(src)
+    # compared by value: a zero key may come out as -0 (the other slots' e^-128 weights are
+    # not zero in double), which e4m3 keeps as code 0x80
+    dec = np.vectorize(oracle.e4m3_value)
+    assert np.array_equal(dec(codes), dec(want.astype(np.uint8)))
