@@ -303,12 +303,33 @@ def run_gpu(args):
     kp_us = timed(g_kp, [g_kp], n_kp) * 1e3
     kp_tokens = kb * P * wl.kpool
     kp_bytes = kp_tokens * (wl.index_dim * 4 + 1) + kb * P * (wl.index_dim * 2 + 1)
+    # fp8 writers: the same pooling stored as fp8 (codes + per-pool scale), and the latent
+    # quantizer over a cache of 262,144 bf16 rows of 512 (two 131,072-token contexts).
+    pk8 = torch.empty((kb, P, wl.index_dim), dtype=torch.uint8, device=dev)
+    sc8 = torch.empty((kb, P), dtype=torch.float32, device=dev)
+    kp8_run = lambda: dsa.kpool_compress_fp8(cfg, k, g_, ape, valid, wl.first_key, pk8, sc8, pv)  # noqa: E731
+    kp8_run()
+    g_kp8 = graph_of([kp8_run])
+    kp8_us = timed(g_kp8, [g_kp8], n_kp) * 1e3
+    kp8_bytes = kp_tokens * (wl.index_dim * 4 + 1) + kb * P * (wl.index_dim + 4 + 1)
+    n_lat = 262144
+    lat = (torch.randn((n_lat, 512), device=dev) * 0.5).to(torch.bfloat16)
+    lat_codes = torch.empty((n_lat, 512), dtype=torch.uint8, device=dev)
+    lat_sc = torch.empty((n_lat,), dtype=torch.float32, device=dev)
+    q_run = lambda: dsa.quantize_rows_fp8(lat, lat_codes, lat_sc)  # noqa: E731
+    q_run()
+    g_q = graph_of([q_run])
+    q_us = timed(g_q, [g_q], n_kp) * 1e3
+    q_bytes = n_lat * (512 * 2 + 512 + 4)
+    del lat, lat_codes, lat_sc
     torch.cuda.set_stream(torch.cuda.default_stream())
 
     return {
         "di": di, "alg": alg, "ms_step": ms_step, "pct": pct, "stage_us": stage_us, "reps": reps,
         "n_tokens": n_tokens, "kpool": {"us": kp_us, "tokens": kp_tokens, "bytes": kp_bytes,
                                         "batch": kb},
+        "fp8_writers": {"kpool_us": kp8_us, "kpool_bytes": kp8_bytes, "quant_us": q_us,
+                        "quant_rows": n_lat, "quant_bytes": q_bytes},
     }
 
 
@@ -492,6 +513,22 @@ def main():
             "achieved_GBs": round(kp["bytes"] / (kp["us"] * 1e-6) / 1e9, 1),
             "frac_of_peak_hbm": round(kp["bytes"] / (kp["us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "sequences": kp["batch"],
+        },
+        "fp8_writers": {
+            "kpool_compress_fp8": {
+                "tokens_per_s": round(kp["tokens"] / (res["fp8_writers"]["kpool_us"] * 1e-6), 1),
+                "launch_us": round(res["fp8_writers"]["kpool_us"], 2),
+                "frac_of_peak_hbm": round(res["fp8_writers"]["kpool_bytes"]
+                                          / (res["fp8_writers"]["kpool_us"] * 1e-6) / 1e9
+                                          / PEAK_HBM_GBS, 4)},
+            "quantize_rows_fp8": {
+                "workload": f"{res['fp8_writers']['quant_rows']} latent rows of 512 bf16",
+                "rows_per_s": round(res["fp8_writers"]["quant_rows"]
+                                    / (res["fp8_writers"]["quant_us"] * 1e-6), 1),
+                "launch_us": round(res["fp8_writers"]["quant_us"], 2),
+                "frac_of_peak_hbm": round(res["fp8_writers"]["quant_bytes"]
+                                          / (res["fp8_writers"]["quant_us"] * 1e-6) / 1e9
+                                          / PEAK_HBM_GBS, 4)},
         },
         "cpu_baseline": cpu,
     }

@@ -32,7 +32,8 @@ ERROR_NAMES = {
 }
 EXPORTED = [
     "dsa_last_error", "dsa_version", "dsa_config_validate", "dsa_select_k", "dsa_out_width",
-    "dsa_num_pools", "dsa_kpool_compress", "dsa_compact_pools", "dsa_index_scores",
+    "dsa_num_pools", "dsa_kpool_compress", "dsa_kpool_compress_fp8", "dsa_quantize_rows_fp8",
+    "dsa_compact_pools", "dsa_index_scores",
     "dsa_compact_index_scores",
     "dsa_topk_pools", "dsa_expand_selection", "dsa_topk_expand", "dsa_sparse_mla_decode_workspace",
     "dsa_sparse_mla_decode", "dsa_absorb_q", "dsa_absorb_o", "dsa_f32_to_bf16_rne",
@@ -82,6 +83,8 @@ def lib():
             "dsa_out_width": ([_CFG], _I64),
             "dsa_num_pools": ([_I64, _I64, _I64], _I64),
             "dsa_kpool_compress": ([_CFG, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P], _I),
+            "dsa_kpool_compress_fp8": ([_CFG, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P], _I),
+            "dsa_quantize_rows_fp8": ([_I64, _I, _P, _I, _P, _P, _P], _I),
             "dsa_compact_pools": ([_I, _I, _P, _P, _P, _P], _I),
             "dsa_index_scores": ([_CFG, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P, _P, _P,
                                   _P, _P, _P], _I),
@@ -200,6 +203,52 @@ def kpool_compress(cfg: Config, k, gate, ape, valid, first_key: int = 0, pool_ke
                                     _ptr(ape), _ptr(valid), _ptr(pool_keys), _ptr(pool_valid),
                                     _stream(k)))
     return pool_keys, pool_valid
+
+
+def kpool_compress_fp8(cfg: Config, k, gate, ape, valid, first_key: int = 0, pool_keys=None,
+                       pool_key_scales=None, pool_valid=None):
+    """kpool_compress with fp8 pooled keys: -> (pool_keys [B,P,D] uint8 e4m3 codes,
+    pool_key_scales [B,P] f32, pool_valid [B,P] u8)."""
+    _dev(k, "k", (torch.bfloat16,))
+    B, S, D = k.shape
+    KP = cfg.index_kpool
+    _dev(gate, "gate", (torch.bfloat16,), (B, S, D))
+    _dev(ape, "ape", (torch.float32,), (KP, D))
+    _dev(valid, "valid", (torch.uint8,), (B, S))
+    if D != cfg.index_head_dim:
+        raise ValueError("key width differs from index_head_dim")
+    P = num_pools(S, first_key, KP)
+    if pool_keys is None:
+        pool_keys = torch.empty((B, P, D), dtype=torch.uint8, device=k.device)
+    if pool_key_scales is None:
+        pool_key_scales = torch.empty((B, P), dtype=torch.float32, device=k.device)
+    if pool_valid is None:
+        pool_valid = torch.empty((B, P), dtype=torch.uint8, device=k.device)
+    _dev(pool_keys, "pool_keys", _FP8, (B, P, D))
+    _dev(pool_key_scales, "pool_key_scales", (torch.float32,), (B, P))
+    _dev(pool_valid, "pool_valid", (torch.uint8,), (B, P))
+    _check(lib().dsa_kpool_compress_fp8(ctypes.byref(cfg), B, S, first_key, _ptr(k), _ptr(gate),
+                                        _ptr(ape), _ptr(valid), _ptr(pool_keys),
+                                        _ptr(pool_key_scales), _ptr(pool_valid), _stream(k)))
+    return pool_keys, pool_key_scales, pool_valid
+
+
+def quantize_rows_fp8(src, codes=None, scales=None):
+    """src [..., n] bf16 or f32 -> (codes uint8 [..., n] e4m3, scales f32 [...]), per row
+    scale amax/448."""
+    _dev(src, "src", (torch.bfloat16, torch.float32))
+    n = src.shape[-1]
+    rows = src.numel() // n if n else 0
+    if codes is None:
+        codes = torch.empty(src.shape, dtype=torch.uint8, device=src.device)
+    if scales is None:
+        scales = torch.empty(src.shape[:-1], dtype=torch.float32, device=src.device)
+    _dev(codes, "codes", _FP8, tuple(src.shape))
+    _dev(scales, "scales", (torch.float32,), tuple(src.shape[:-1]))
+    code = DSA_F32 if src.dtype == torch.float32 else DSA_BF16
+    _check(lib().dsa_quantize_rows_fp8(rows, n, _ptr(src), code, _ptr(codes), _ptr(scales),
+                                       _stream(src)))
+    return codes, scales
 
 
 def compact_pools(pool_valid, ids=None, n_valid=None):

@@ -145,9 +145,50 @@ int dsa_kpool_compress(const dsa_config *cfg, int B, int S, int first_key, const
     return hip_status(dsa::launch_kpool_compress(B, S, D, cfg->index_kpool, first_key, (int)P,
                                                  static_cast<const uint16_t *>(k),
                                                  static_cast<const uint16_t *>(gate), ape, valid,
-                                                 static_cast<uint16_t *>(pool_keys), pool_valid,
-                                                 stream),
+                                                 pool_keys, nullptr, pool_valid, stream),
                       "kpool_compress launch");
+}
+
+int dsa_kpool_compress_fp8(const dsa_config *cfg, int B, int S, int first_key, const void *k,
+                           const void *gate, const float *ape, const uint8_t *valid,
+                           uint8_t *pool_keys, float *pool_key_scales, uint8_t *pool_valid,
+                           hipStream_t stream) {
+    clear_error();
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    const int D = cfg->index_head_dim;
+    if (D < 8 || D > 512 || (D & (D - 1)) != 0)
+        return set_error(DSA_ERR_UNSUPPORTED, "kpool_compress_fp8: index_head_dim %d must be a power of two in [8, 512]", D);
+    if (B < 0 || S < 0 || first_key < 0) return set_error(DSA_ERR_BAD_SIZE, "negative B, S or first_key");
+    const int64_t P = num_pools(S, first_key, cfg->index_kpool);
+    if ((int64_t)B * P == 0) return DSA_OK;
+    if (!k || !gate || !ape || !valid || !pool_keys || !pool_key_scales || !pool_valid)
+        return set_error(DSA_ERR_NULL_ARG, "kpool_compress_fp8: a buffer is NULL");
+    if (!aligned(k, 16) || !aligned(gate, 16) || !aligned(pool_keys, 8) || !aligned(ape, 16))
+        return set_error(DSA_ERR_BAD_SIZE, "kpool_compress_fp8: k, gate and ape need 16-byte alignment, pool_keys 8-byte");
+    return hip_status(dsa::launch_kpool_compress(B, S, D, cfg->index_kpool, first_key, (int)P,
+                                                 static_cast<const uint16_t *>(k),
+                                                 static_cast<const uint16_t *>(gate), ape, valid,
+                                                 pool_keys, pool_key_scales, pool_valid, stream),
+                      "kpool_compress_fp8 launch");
+}
+
+int dsa_quantize_rows_fp8(int64_t rows, int n, const void *src, dsa_dtype src_dtype, uint8_t *codes,
+                          float *scales, hipStream_t stream) {
+    clear_error();
+    if (rows < 0 || n <= 0) return set_error(DSA_ERR_BAD_SIZE, "quantize_rows_fp8: rows >= 0 and n > 0 needed");
+    if (n % 8 != 0 || n > 4096)
+        return set_error(DSA_ERR_UNSUPPORTED, "quantize_rows_fp8: n = %d must be a multiple of 8 up to 4096", n);
+    if (src_dtype != DSA_BF16 && src_dtype != DSA_F32)
+        return set_error(DSA_ERR_BAD_DTYPE, "quantize_rows_fp8: source must be bf16 or f32");
+    if (rows > INT32_MAX) return set_error(DSA_ERR_UNSUPPORTED, "quantize_rows_fp8: rows above 2^31 - 1");
+    if (rows == 0) return DSA_OK;
+    if (!src || !codes || !scales) return set_error(DSA_ERR_NULL_ARG, "quantize_rows_fp8: a buffer is NULL");
+    if (!aligned(src, 16) || !aligned(codes, 8))
+        return set_error(DSA_ERR_BAD_SIZE, "quantize_rows_fp8: src needs 16-byte and codes 8-byte alignment");
+    return hip_status(dsa::launch_quantize_rows((long long)rows, n, src, src_dtype == DSA_F32, codes,
+                                                scales, stream),
+                      "quantize_rows_fp8 launch");
 }
 
 int dsa_compact_pools(int B, int P, const uint8_t *pool_valid, int32_t *ids, int32_t *n_valid,

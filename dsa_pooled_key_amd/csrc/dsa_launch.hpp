@@ -10,10 +10,14 @@
 
 namespace dsa {
 
+// key_scales NULL: bf16 pooled keys; else fp8 e4m3 pooled keys with per-pool f32 scales.
 hipError_t launch_kpool_compress(int B, int S, int D, int KP, int first_key, int P,
                                  const uint16_t *k, const uint16_t *gate, const float *ape,
-                                 const uint8_t *valid, uint16_t *pool_keys, uint8_t *pool_valid,
-                                 hipStream_t stream);
+                                 const uint8_t *valid, void *pool_keys, float *key_scales,
+                                 uint8_t *pool_valid, hipStream_t stream);
+// Rows of n values (bf16 or f32) -> e4m3 codes and per-row f32 scales.
+hipError_t launch_quantize_rows(long long rows, int n, const void *src, bool f32_src,
+                                uint8_t *codes, float *scales, hipStream_t stream);
 
 hipError_t launch_compact_pools(int B, int P, const uint8_t *pool_valid, int32_t *ids,
                                 int32_t *n_valid, hipStream_t stream);

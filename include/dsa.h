@@ -129,6 +129,28 @@ int dsa_kpool_compress(const dsa_config *cfg, int B, int S, int first_key, const
                        const void *gate, const float *ape, const uint8_t *valid, void *pool_keys,
                        uint8_t *pool_valid, hipStream_t stream);
 
+/* The stored fp8 form of fp8 pooled keys and latent rows (the pages keep the selected tokens
+ * in fp8 for the serve's decode, mod.rs MASKED_ATTN_MAX_KEYS; the per-row format is this
+ * library's reading): per row, scale = amax / 448 with amax the largest |value| of the row
+ * (1 for an all-zero row), and each value stored as the OCP e4m3 code nearest to
+ * value / scale (ties to even, saturating at +-448); both divisions in IEEE single
+ * precision, so the row decodes as code * scale.
+ *
+ * dsa_kpool_compress with the pooled key stored that way: the bf16 pooled key of
+ * dsa_kpool_compress, quantized per pool row. pool_keys: [B, P, D] e4m3 codes (8-byte
+ * aligned); pool_key_scales: [B, P] f32; pool_valid as dsa_kpool_compress. D must be a power
+ * of two in [8, 512] (DSA_ERR_UNSUPPORTED otherwise). */
+int dsa_kpool_compress_fp8(const dsa_config *cfg, int B, int S, int first_key, const void *k,
+                           const void *gate, const float *ape, const uint8_t *valid,
+                           uint8_t *pool_keys, float *pool_key_scales, uint8_t *pool_valid,
+                           hipStream_t stream);
+
+/* Rows of n values quantized as above: src [rows, n] bf16 or f32 (src_dtype, 16-byte
+ * aligned), codes [rows, n] e4m3 (8-byte aligned), scales [rows] f32. n must be a multiple
+ * of 8 up to 4096 (DSA_ERR_UNSUPPORTED). For the latent cache n = 512. */
+int dsa_quantize_rows_fp8(int64_t rows, int n, const void *src, dsa_dtype src_dtype, uint8_t *codes,
+                          float *scales, hipStream_t stream);
+
 /* ------------------------------------------------------------------ step 2 */
 /* mod.rs names dsa_compact_pools between pooling and scoring. Stable compaction per
  * sequence: ids[b, 0..n_valid[b]) are the valid pool indices in ascending order, the rest of

@@ -457,6 +457,76 @@ def test_kpool_compress(name, exact):
     assert not bad.any(), (np.argwhere(bad)[:4], a[bad][:4], b[bad][:4])
 
 
+@pytest.mark.parametrize("exact", [False, True])
+@pytest.mark.parametrize("name", ALL)
+def test_kpool_compress_fp8(name, exact):
+    """fp8 pooled keys: the GPU's own bf16 pooled key (the bf16 launch, same arithmetic)
+    quantized by the oracle's quantizer gives the fp8 launch's codes and scales bit for bit;
+    on the exact twins the codes equal the oracle's whole fp8 pooling by value (+-0 alike)."""
+    ki = synth.make_kpool_inputs(name, exact=exact, batch=KPOOL_BATCH.get(name))
+    wl = ki.wl
+    cfg = config_for(wl)
+    k = _dev(ki.k.view(np.int16)).view(torch.bfloat16)
+    g = _dev(ki.gate.view(np.int16)).view(torch.bfloat16)
+    ape, valid = _dev(ki.ape), _dev(ki.valid)
+    pk, pv = dsa.kpool_compress(cfg, k, g, ape, valid, wl.first_key)
+    codes, sc, pv8 = dsa.kpool_compress_fp8(cfg, k, g, ape, valid, wl.first_key)
+    assert torch.equal(pv, pv8)
+    gvals = synth.bf16_to_f32(pk.view(torch.int16).cpu().numpy().view(np.uint16))
+    rc, rs = oracle.quantize_rows(gvals)
+    assert np.array_equal(sc.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    if exact:
+        oc, osc, opv = oracle.kpool_compress_fp8(ki.k, ki.gate, ki.ape, ki.valid, wl.kpool,
+                                                 wl.first_key)
+        assert np.array_equal(pv8.cpu().numpy(), opv)
+        assert np.array_equal(sc.cpu().numpy(), osc)
+        dec = np.vectorize(oracle.e4m3_value, otypes=[np.float64])
+        got = codes.cpu().numpy()
+        lut = dec(np.arange(256, dtype=np.uint8))
+        assert np.array_equal(lut[got], lut[oc])
+
+
+def _quant_rows_case(n, rng):
+    rows = [rng.standard_normal(n) * 0.5,
+            np.zeros(n),
+            np.where(np.arange(n) == 3, -2.75, 0.0),
+            rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n)),     # wide range
+            rng.standard_normal(n) * 1e-3]
+    # s = 1 (amax 448): every other value a midpoint between two e4m3 values (ties to even)
+    vals = np.array([oracle.e4m3_value(c) for c in range(0x7f)])
+    mids = (vals[:-1] + vals[1:]) / 2
+    t = rng.choice(mids, n) * rng.choice([-1.0, 1.0], n)
+    t[0] = 448.0
+    rows.append(t)
+    neg0 = np.full(n, -0.0)
+    neg0[1] = 1.0
+    rows.append(neg0)
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("n", [8, 72, 512, 4096])
+def test_quantize_rows_fp8_bit_exact(n):
+    """Latent-row quantizer, bf16 and f32 sources: codes and scales bit-exact with the
+    oracle, on random rows, zero rows, a single nonzero, a 2^+-30 dynamic range, values in
+    the subnormal range, exact midpoints (ties to even) and negative zeros; also 1200 rows of
+    512 (the latent width) drawn like the latent cache."""
+    rng = np.random.default_rng(n)
+    x = _quant_rows_case(n, rng)
+    if n == 512:
+        x = np.concatenate([x, (rng.standard_normal((1200, n)) * 0.5).astype(np.float32)])
+    for src in (x, synth.bf16_to_f32(synth.bf16_bits(x))):
+        rc, rs = oracle.quantize_rows(src)
+        for dt in ((torch.float32,) if src is x else (torch.bfloat16, torch.float32)):
+            t = torch.from_numpy(src).cuda().to(dt)
+            codes, sc = dsa.quantize_rows_fp8(t)
+            assert np.array_equal(sc.cpu().numpy(), rs), dt
+            got = codes.cpu().numpy()
+            bad = np.argwhere(got != rc)
+            assert bad.size == 0, (dt, bad[:5], got[tuple(bad[0])], rc[tuple(bad[0])],
+                                   src[tuple(bad[0])] / rs[bad[0][0]])
+
+
 # ------------------------------------------------------------------ chains
 
 def _oracle_select(di, ids, nv, rows):
