@@ -68,6 +68,14 @@ def lib():
         L.orc_sparse_mla.argtypes = [_I, _I, _I, _I, _D, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I,
                                      _P, _P]
         L.orc_sparse_mla.restype = None
+        L.orc_layer_norm.argtypes = [_L, _I, _P, _P, _P, _D]
+        L.orc_layer_norm.restype = None
+        L.orc_indexer_store.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _P]
+        L.orc_indexer_store.restype = None
+        L.orc_write_geom.argtypes = [_I, _P, _P, _P]
+        L.orc_write_geom.restype = None
+        L.orc_pool_append.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+        L.orc_pool_append.restype = None
         L.orc_e4m3_from_float.argtypes = [ctypes.c_float]
         L.orc_e4m3_from_float.restype = ctypes.c_uint8
         L.orc_quantize_rows.argtypes = [_L, _I, _P, _P, _P]
@@ -168,6 +176,65 @@ def kpool_compress_fp8(k, gate, ape, valid, kpool: int, first_key: int):
     vals = (pk.astype(np.uint32) << 16).view(np.float32)
     codes, scales = quantize_rows(vals)
     return codes, scales, pv
+
+
+def layer_norm(x, weight, bias, eps: float = 1e-5):
+    """LayerNorm with a bias over the last axis of bf16 rows (k_norm): x [..., D] bf16 bits,
+    weight/bias [D] bf16 bits -> new bf16 bits array (the input is not modified)."""
+    x = np.array(x, np.uint16, copy=True, order="C")
+    D = x.shape[-1]
+    weight = _arr(weight, np.uint16, (D,), "weight")
+    bias = _arr(bias, np.uint16, (D,), "bias")
+    rows = x.size // D if D else 0
+    if rows:
+        lib().orc_layer_norm(rows, D, _ptr(x), _ptr(weight), _ptr(bias), float(eps))
+    return x
+
+
+def indexer_store(pos, k_row, gate_row, k_cache, gate_cache, valid):
+    """Returns updated copies (k_cache, gate_cache, valid) after storing each sequence's staged
+    row at pos[b] (when 0 <= pos[b] < S) and marking it valid."""
+    k_cache = np.array(k_cache, np.uint16, copy=True, order="C")
+    B, S, D = k_cache.shape
+    gate_cache = np.array(gate_cache, np.uint16, copy=True, order="C").reshape(B, S, D)
+    valid = np.array(valid, np.uint8, copy=True, order="C").reshape(B, S)
+    pos = _arr(pos, np.int32, (B,), "pos")
+    k_row = _arr(k_row, np.uint16, (B, D), "k_row")
+    gate_row = _arr(gate_row, np.uint16, (B, D), "gate_row")
+    lib().orc_indexer_store(B, S, D, _ptr(pos), _ptr(k_row), _ptr(gate_row), _ptr(k_cache),
+                            _ptr(gate_cache), _ptr(valid))
+    return k_cache, gate_cache, valid
+
+
+def write_geom(seq_len):
+    """Decode geometry from the live lengths: (row_seq [B], row_pos [B]) int32."""
+    seq_len = _arr(seq_len, np.int32, name="seq_len")
+    B = seq_len.shape[0]
+    rs = np.zeros(B, np.int32)
+    rp = np.zeros(B, np.int32)
+    lib().orc_write_geom(B, _ptr(seq_len), _ptr(rs), _ptr(rp))
+    return rs, rp
+
+
+def pool_append(pos, k, gate, ape, valid, pool_keys, pool_valid, ids, n_valid, *, kpool: int,
+                first_key: int):
+    """The pool each sequence's new token (at pos[b]) completes: its key and validity as
+    kpool_compress computes them, and, when valid, its id appended to the compacted list.
+    Returns updated copies (pool_keys, pool_valid, ids, n_valid)."""
+    k = _arr(k, np.uint16, name="k")
+    B, S, D = k.shape
+    gate = _arr(gate, np.uint16, (B, S, D), "gate")
+    ape = _arr(ape, np.float32, (kpool, D), "ape")
+    valid = _arr(valid, np.uint8, (B, S), "valid")
+    P = num_pools(S, first_key, kpool)
+    pos = _arr(pos, np.int32, (B,), "pos")
+    pk = np.array(pool_keys, np.uint16, copy=True, order="C").reshape(B, P, D)
+    pv = np.array(pool_valid, np.uint8, copy=True, order="C").reshape(B, P)
+    ids = np.array(ids, np.int32, copy=True, order="C").reshape(B, P)
+    nv = np.array(n_valid, np.int32, copy=True, order="C").reshape(B)
+    lib().orc_pool_append(B, S, D, kpool, first_key, _ptr(pos), _ptr(k), _ptr(gate), _ptr(ape),
+                          _ptr(valid), _ptr(pk), _ptr(pv), _ptr(ids), _ptr(nv))
+    return pk, pv, ids, nv
 
 
 def compact_pools(pool_valid):

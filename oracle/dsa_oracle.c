@@ -174,14 +174,26 @@ void orc_quantize_rows(long rows, int n, const float *x, uint8_t *codes, float *
  * identity (its first token is first_key + p*KP), so no separate index array is written.
  * Layouts: k, gate [B,S,D] bf16; ape [KP,D] f32; valid [B,S] u8;
  * pool_keys [B,P,D] bf16; pool_valid [B,P] u8, with P = orc_num_pools(S, first_key, KP). */
+static void compress_pool(long b, long p, long P, int S, int D, int KP, int first_key,
+                          const uint16_t *k, const uint16_t *gate, const float *ape,
+                          const uint8_t *valid, uint16_t *pool_keys, uint8_t *pool_valid);
+
 void orc_kpool_compress(int B, int S, int D, int KP, int first_key,
                         const uint16_t *k, const uint16_t *gate, const float *ape,
                         const uint8_t *valid, uint16_t *pool_keys, uint8_t *pool_valid) {
     long P = orc_num_pools(S, first_key, KP);
     long bp;
 #pragma omp parallel for schedule(static)
-    for (bp = 0; bp < (long)B * P; ++bp) {
-        long b = bp / P, p = bp % P;
+    for (bp = 0; bp < (long)B * P; ++bp)
+        compress_pool(bp / P, bp % P, P, S, D, KP, first_key, k, gate, ape, valid, pool_keys,
+                      pool_valid);
+}
+
+/* Pool p of sequence b (the body of orc_kpool_compress). */
+static void compress_pool(long b, long p, long P, int S, int D, int KP, int first_key,
+                          const uint16_t *k, const uint16_t *gate, const float *ape,
+                          const uint8_t *valid, uint16_t *pool_keys, uint8_t *pool_valid) {
+    {
         long t0 = (long)first_key + p * KP;
         int ok = 1;
         for (int s = 0; s < KP; ++s)
@@ -419,6 +431,88 @@ void orc_sparse_mla(int Q, int H, int C, int W, double sm, const uint16_t *q_abs
         free(rows);
         free(logit);
         free(v);
+    }
+}
+
+/* ---------------------------------------------------------------- decode-time cache maintenance */
+
+/* mod.rs, Glm5NextDsaKernels::k_norm: indexer.k_norm is a LayerNorm with a bias (not an
+ * RMSNorm), applied in place to bf16 rows with bf16 weight and bias.
+ * Reading: per row the mean and the biased variance over the D values;
+ * y = (x - mean) / sqrt(var + eps) * weight + bias, in double, rounded once to bf16.
+ * Layouts: x [rows, D] bf16 (in place); weight, bias [D] bf16. */
+void orc_layer_norm(long rows, int D, uint16_t *x, const uint16_t *weight, const uint16_t *bias,
+                    double eps) {
+    for (long r = 0; r < rows; ++r) {
+        uint16_t *row = x + r * D;
+        double mean = 0.0, var = 0.0;
+        for (int d = 0; d < D; ++d) mean += bf16_value(row[d]);
+        mean /= D;
+        for (int d = 0; d < D; ++d) var += (bf16_value(row[d]) - mean) * (bf16_value(row[d]) - mean);
+        var /= D;
+        double inv = 1.0 / sqrt(var + eps);
+        for (int d = 0; d < D; ++d)
+            row[d] = bf16_from_float(
+                (float)((bf16_value(row[d]) - mean) * inv * bf16_value(weight[d]) + bf16_value(bias[d])));
+    }
+}
+
+/* mod.rs, Glm5NextDsaKernels::indexer_store: the staged indexer row is copied to a device-side
+ * position and marked valid.
+ * Reading: the staged row of sequence b is its new token's key and gate; for
+ * 0 <= pos[b] < S: k_cache[b,pos] = k_row[b], gate_cache[b,pos] = gate_row[b],
+ * valid[b,pos] = 1; any other pos stores nothing.
+ * Layouts: pos [B] i32; k_row, gate_row [B, D] bf16; k_cache, gate_cache [B, S, D] bf16;
+ * valid [B, S] u8. */
+void orc_indexer_store(int B, int S, int D, const int32_t *pos, const uint16_t *k_row,
+                       const uint16_t *gate_row, uint16_t *k_cache, uint16_t *gate_cache,
+                       uint8_t *valid) {
+    for (long b = 0; b < B; ++b) {
+        long t = pos[b];
+        if (t < 0 || t >= S) continue;
+        for (int d = 0; d < D; ++d) {
+            k_cache[(b * S + t) * D + d] = k_row[b * D + d];
+            gate_cache[(b * S + t) * D + d] = gate_row[b * D + d];
+        }
+        valid[b * S + t] = 1;
+    }
+}
+
+/* mod.rs, Glm5NextDsaKernels::write_geom: the selector geometry derived on the device from
+ * seq_len, so a captured graph replays over the live context.
+ * Reading (decode, one query row per sequence): row_seq[b] = b, row_pos[b] = seq_len[b] - 1. */
+void orc_write_geom(int B, const int32_t *seq_len, int32_t *row_seq, int32_t *row_pos) {
+    for (int b = 0; b < B; ++b) {
+        row_seq[b] = b;
+        row_pos[b] = seq_len[b] - 1;
+    }
+}
+
+/* The pool that a newly stored token completes, kept up to date at decode time (mod.rs
+ * "Checkpoint and kernel facts": pooling starts at first_key and a pool counts only when
+ * all its slots are valid; "Shape of the pipeline": pool keys, indices and validity).
+ * Reading: token pos of sequence b completes pool p = (pos - first_key + 1)/KP - 1 when
+ * pos >= first_key, (pos - first_key + 1) % KP == 0 and p < P. That pool's key and validity
+ * are computed exactly as kpool_compress computes them, and a valid pool is appended to the
+ * compacted id list (ids[b, n_valid[b]] = p, n_valid[b] += 1) unless the list already ends at
+ * p or beyond; any other position changes nothing.
+ * Layouts as orc_kpool_compress and orc_compact_pools; pos [B] i32. */
+void orc_pool_append(int B, int S, int D, int KP, int first_key, const int32_t *pos,
+                     const uint16_t *k, const uint16_t *gate, const float *ape,
+                     const uint8_t *valid, uint16_t *pool_keys, uint8_t *pool_valid,
+                     int32_t *ids, int32_t *n_valid) {
+    long P = orc_num_pools(S, first_key, KP);
+    for (long b = 0; b < B; ++b) {
+        long t = pos[b];
+        if (t < first_key || t >= S || (t - first_key + 1) % KP != 0) continue;
+        long p = (t - first_key + 1) / KP - 1;
+        if (p >= P) continue;
+        compress_pool(b, p, P, S, D, KP, first_key, k, gate, ape, valid, pool_keys, pool_valid);
+        long n = n_valid[b];
+        if (pool_valid[b * P + p] && (n == 0 || ids[b * P + n - 1] < p) && n < P) {
+            ids[b * P + n] = (int32_t)p;
+            n_valid[b] = (int32_t)(n + 1);
+        }
     }
 }
 

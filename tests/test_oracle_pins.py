@@ -761,3 +761,87 @@ def test_kpool_compress_fp8_is_the_bf16_pooled_key_quantized():
     # not zero in double), which e4m3 keeps as code 0x80
     dec = np.vectorize(oracle.e4m3_value)
     assert np.array_equal(dec(codes), dec(want.astype(np.uint8)))
+
+
+# ------------------------------------------------------------------ decode-time cache maintenance
+
+def test_layer_norm_matches_torch_and_keeps_the_bias():
+    """k_norm is a LayerNorm with a bias: the oracle equals torch's layer_norm in float64 up to
+    the final bf16 rounding; a constant row gives the bias exactly; shifting a row by a
+    constant changes nothing (the mean is subtracted, unlike an RMSNorm)."""
+    rng = np.random.default_rng(50)
+    rows, D = 40, 128
+    x = synth.bf16_bits((rng.standard_normal((rows, D)) * 2 + rng.standard_normal((rows, 1)) * 3).astype(np.float32))
+    w = synth.bf16_bits((1 + 0.2 * rng.standard_normal(D)).astype(np.float32))
+    b = synth.bf16_bits((0.1 * rng.standard_normal(D)).astype(np.float32))
+    eps = 1e-5
+    x0 = x.copy()
+    y = oracle.layer_norm(x, w, b, eps)
+    assert np.array_equal(x, x0)  # the input is not modified
+    ref = torch.nn.functional.layer_norm(
+        torch.from_numpy(synth.bf16_to_f32(x).astype(np.float64)), (D,),
+        torch.from_numpy(synth.bf16_to_f32(w).astype(np.float64)),
+        torch.from_numpy(synth.bf16_to_f32(b).astype(np.float64)), eps).numpy()
+    got = synth.bf16_to_f32(y).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 0.5 * bf16_ulp(ref) + 1e-12)
+    const = np.tile(synth.bf16_bits(np.float32(1.5)), (3, D))
+    assert np.array_equal(oracle.layer_norm(const, w, b, eps), np.tile(b, (3, 1)))
+    # dyadic rows shifted by 4: the same bf16 values in and out
+    xd = synth.bf16_bits((rng.integers(-16, 17, (6, D)) / 8.0).astype(np.float32))
+    xs = synth.bf16_bits(synth.bf16_to_f32(xd) + np.float32(4.0))
+    assert np.array_equal(oracle.layer_norm(xd, w, b, eps), oracle.layer_norm(xs, w, b, eps))
+
+
+def test_indexer_store_and_write_geom_by_enumeration():
+    rng = np.random.default_rng(51)
+    B, S, D = 4, 9, 16
+    k_cache = rng.integers(0, 65535, (B, S, D)).astype(np.uint16)
+    g_cache = rng.integers(0, 65535, (B, S, D)).astype(np.uint16)
+    valid = (rng.random((B, S)) > 0.5).astype(np.uint8)
+    kr = rng.integers(0, 65535, (B, D)).astype(np.uint16)
+    gr = rng.integers(0, 65535, (B, D)).astype(np.uint16)
+    pos = np.array([0, 8, 9, -1], np.int32)  # the last two are out of range
+    k2, g2, v2 = oracle.indexer_store(pos, kr, gr, k_cache, g_cache, valid)
+    for b in range(B):
+        for t in range(S):
+            hit = t == pos[b]
+            assert np.array_equal(k2[b, t], kr[b] if hit else k_cache[b, t])
+            assert np.array_equal(g2[b, t], gr[b] if hit else g_cache[b, t])
+            assert v2[b, t] == (1 if hit else valid[b, t])
+    rs, rp = oracle.write_geom(np.array([5, 1, 100, 0], np.int32))
+    assert list(rs) == [0, 1, 2, 3] and list(rp) == [4, 0, 99, -1]
+
+
+@pytest.mark.parametrize("kp,f", [(4, 0), (8, 5), (3, 2), (1, 0)])
+def test_pool_append_token_by_token_equals_the_batch_pooling(kp, f):
+    """Storing a sequence's tokens one at a time and appending each pool as its last slot
+    lands gives the batch kpool_compress keys and validity and the compact_pools id list;
+    appending the same position twice changes nothing; a position inside a pool changes
+    nothing."""
+    rng = np.random.default_rng(52 + kp)
+    B, S, D = 3, 45, 16
+    k = synth.bf16_bits(rng.standard_normal((B, S, D)).astype(np.float32))
+    gate = synth.bf16_bits(rng.standard_normal((B, S, D)).astype(np.float32))
+    ape = rng.standard_normal((kp, D)).astype(np.float32)
+    final_valid = (rng.random((B, S)) > 0.08).astype(np.uint8)
+    P = oracle.num_pools(S, f, kp)
+    kc = np.zeros_like(k)
+    gc = np.zeros_like(gate)
+    vc = np.zeros((B, S), np.uint8)
+    pk = np.zeros((B, P, D), np.uint16)
+    pv = np.zeros((B, P), np.uint8)
+    ids = np.full((B, P), -1, np.int32)
+    nv = np.zeros(B, np.int32)
+    for t in range(S):
+        pos = np.full(B, t, np.int32)
+        kc, gc, vc = oracle.indexer_store(pos, k[:, t], gate[:, t], kc, gc, vc)
+        vc[:, t] = final_valid[:, t]          # a token may arrive masked
+        pk, pv, ids, nv = oracle.pool_append(pos, kc, gc, ape, vc, pk, pv, ids, nv, kpool=kp,
+                                             first_key=f)
+        pk2, pv2, ids2, nv2 = oracle.pool_append(pos, kc, gc, ape, vc, pk, pv, ids, nv, kpool=kp,
+                                                 first_key=f)
+        assert np.array_equal(ids2, ids) and np.array_equal(nv2, nv)
+    rk, rv = oracle.kpool_compress(k, gate, ape, final_valid, kp, f)
+    rids, rnv = oracle.compact_pools(rv)
+    assert np.array_equal(pv, rv) and np.array_equal(pk, rk)
+    assert np.array_equal(ids, rids) and np.array_equal(nv, rnv)
