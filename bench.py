@@ -251,6 +251,20 @@ def run_gpu(args):
         g_single[i % reps].replay()
     torch.cuda.synchronize()
 
+    def per_launch_us(fn, in_graph, replays):
+        """One graph of in_graph launches of fn, replayed; microseconds per launch (the
+        graph launch overhead spread over in_graph kernels)."""
+        g = graph_of([fn] * in_graph)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(replays):
+            g.replay()
+        b.record(stream)
+        b.synchronize()
+        return a.elapsed_time(b) / (in_graph * replays) * 1e3
+
     def timed(cycle_graph, single_graphs, k):
         """Replay exactly k launches of the recorded work, rotating replicas; ms per one."""
         full, rest = divmod(k, len(single_graphs))
@@ -298,9 +312,8 @@ def run_gpu(args):
     cfg = steps[0].cfg
     kp_run = lambda: dsa.kpool_compress(cfg, k, g_, ape, valid, wl.first_key, pk, pv)  # noqa: E731
     kp_run()
-    g_kp = graph_of([kp_run])
-    n_kp = max(5, args.steps // 10)
-    kp_us = timed(g_kp, [g_kp], n_kp) * 1e3
+    n_kp = max(5, args.steps // 40)
+    kp_us = per_launch_us(kp_run, 4, n_kp)
     kp_tokens = kb * P * wl.kpool
     kp_bytes = kp_tokens * (wl.index_dim * 4 + 1) + kb * P * (wl.index_dim * 2 + 1)
     # fp8 writers: the same pooling stored as fp8 (codes + per-pool scale), and the latent
@@ -309,8 +322,7 @@ def run_gpu(args):
     sc8 = torch.empty((kb, P), dtype=torch.float32, device=dev)
     kp8_run = lambda: dsa.kpool_compress_fp8(cfg, k, g_, ape, valid, wl.first_key, pk8, sc8, pv)  # noqa: E731
     kp8_run()
-    g_kp8 = graph_of([kp8_run])
-    kp8_us = timed(g_kp8, [g_kp8], n_kp) * 1e3
+    kp8_us = per_launch_us(kp8_run, 4, n_kp)
     kp8_bytes = kp_tokens * (wl.index_dim * 4 + 1) + kb * P * (wl.index_dim + 4 + 1)
     n_lat = 262144
     lat = (torch.randn((n_lat, 512), device=dev) * 0.5).to(torch.bfloat16)
@@ -318,16 +330,40 @@ def run_gpu(args):
     lat_sc = torch.empty((n_lat,), dtype=torch.float32, device=dev)
     q_run = lambda: dsa.quantize_rows_fp8(lat, lat_codes, lat_sc)  # noqa: E731
     q_run()
-    g_q = graph_of([q_run])
-    q_us = timed(g_q, [g_q], n_kp) * 1e3
+    q_us = per_launch_us(q_run, 4, n_kp)
     q_bytes = n_lat * (512 * 2 + 512 + 4)
     del lat, lat_codes, lat_sc
+    # Decode-time upkeep of the same token cache (one new token per sequence, each at a
+    # position that completes a pool): k_norm of the staged key rows, indexer_store,
+    # write_geom and pool_append (fp8 keys). Small latency-bound launches.
+    f, kpl = wl.first_key, wl.kpool
+    up_pos = torch.tensor([f + ((S - 1 - f) // kpl - 1 - 3 * i) * kpl + kpl - 1 for i in range(kb)],
+                          dtype=torch.int32, device=dev)
+    k_rows = k[:, 0].contiguous()
+    g_rows = g_[:, 0].contiguous()
+    ln_w = torch.ones((wl.index_dim,), dtype=torch.bfloat16, device=dev)
+    ln_b = torch.zeros((wl.index_dim,), dtype=torch.bfloat16, device=dev)
+    seq_len = up_pos + 1
+    rs_, rp_ = torch.empty_like(up_pos), torch.empty_like(up_pos)
+    ids_, nv_ = dsa.compact_pools(pv)
+    upkeep = {
+        "k_norm": lambda: dsa.k_norm(k_rows, ln_w, ln_b, 1e-5),
+        "indexer_store": lambda: dsa.indexer_store(up_pos, k_rows, g_rows, k, g_, valid),
+        "write_geom": lambda: dsa.write_geom(seq_len, rs_, rp_),
+        "pool_append": lambda: dsa.pool_append(cfg, up_pos, k, g_, ape, valid, pk8, pv, ids_, nv_,
+                                               first_key=f, pool_key_scales=sc8),
+    }
+    up_us = {}
+    for nm, fn in upkeep.items():
+        fn()
+        up_us[nm] = per_launch_us(fn, 50, 10)
     torch.cuda.set_stream(torch.cuda.default_stream())
 
     return {
         "di": di, "alg": alg, "ms_step": ms_step, "pct": pct, "stage_us": stage_us, "reps": reps,
         "n_tokens": n_tokens, "kpool": {"us": kp_us, "tokens": kp_tokens, "bytes": kp_bytes,
                                         "batch": kb},
+        "upkeep_us": up_us, "upkeep_batch": kb,
         "fp8_writers": {"kpool_us": kp8_us, "kpool_bytes": kp8_bytes, "quant_us": q_us,
                         "quant_rows": n_lat, "quant_bytes": q_bytes},
     }
@@ -529,6 +565,11 @@ def main():
                 "frac_of_peak_hbm": round(res["fp8_writers"]["quant_bytes"]
                                           / (res["fp8_writers"]["quant_us"] * 1e-6) / 1e9
                                           / PEAK_HBM_GBS, 4)},
+        },
+        "decode_upkeep": {
+            "workload": f"one new token in each of {res['upkeep_batch']} sequences of the "
+                        f"{wl.name} token cache, each completing a pool (fp8 pooled keys)",
+            "launch_us": {k_: round(v_, 2) for k_, v_ in res["upkeep_us"].items()},
         },
         "cpu_baseline": cpu,
     }

@@ -33,6 +33,7 @@ ERROR_NAMES = {
 EXPORTED = [
     "dsa_last_error", "dsa_version", "dsa_config_validate", "dsa_select_k", "dsa_out_width",
     "dsa_num_pools", "dsa_kpool_compress", "dsa_kpool_compress_fp8", "dsa_quantize_rows_fp8",
+    "dsa_k_norm", "dsa_indexer_store", "dsa_write_geom", "dsa_pool_append",
     "dsa_compact_pools", "dsa_index_scores",
     "dsa_compact_index_scores",
     "dsa_topk_pools", "dsa_expand_selection", "dsa_topk_expand", "dsa_sparse_mla_decode_workspace",
@@ -85,6 +86,10 @@ def lib():
             "dsa_kpool_compress": ([_CFG, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P], _I),
             "dsa_kpool_compress_fp8": ([_CFG, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P], _I),
             "dsa_quantize_rows_fp8": ([_I64, _I, _P, _I, _P, _P, _P], _I),
+            "dsa_k_norm": ([_I64, _I, _P, _P, _P, _F, _P], _I),
+            "dsa_indexer_store": ([_I, _I, _I, _P, _P, _P, _P, _P, _P, _P], _I),
+            "dsa_write_geom": ([_I, _P, _P, _P, _P], _I),
+            "dsa_pool_append": ([_CFG, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
             "dsa_compact_pools": ([_I, _I, _P, _P, _P, _P], _I),
             "dsa_index_scores": ([_CFG, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P, _P, _P,
                                   _P, _P, _P], _I),
@@ -249,6 +254,72 @@ def quantize_rows_fp8(src, codes=None, scales=None):
     _check(lib().dsa_quantize_rows_fp8(rows, n, _ptr(src), code, _ptr(codes), _ptr(scales),
                                        _stream(src)))
     return codes, scales
+
+
+def k_norm(x, weight, bias, eps: float = 1e-5):
+    """indexer.k_norm, a LayerNorm with a bias, in place on x [..., D] bf16; returns x."""
+    _dev(x, "x", (torch.bfloat16,))
+    D = x.shape[-1]
+    _dev(weight, "weight", (torch.bfloat16,), (D,))
+    _dev(bias, "bias", (torch.bfloat16,), (D,))
+    rows = x.numel() // D if D else 0
+    _check(lib().dsa_k_norm(rows, D, _ptr(x), _ptr(weight), _ptr(bias), float(eps), _stream(x)))
+    return x
+
+
+def indexer_store(pos, k_row, gate_row, k_cache, gate_cache, valid):
+    """Staged rows k_row/gate_row [B,D] bf16 to position pos[b] of k_cache/gate_cache
+    [B,S,D], marking valid [B,S]; all in place."""
+    _dev(k_cache, "k_cache", (torch.bfloat16,))
+    B, S, D = k_cache.shape
+    _dev(gate_cache, "gate_cache", (torch.bfloat16,), (B, S, D))
+    _dev(valid, "valid", (torch.uint8,), (B, S))
+    _dev(pos, "pos", (torch.int32,), (B,))
+    _dev(k_row, "k_row", (torch.bfloat16,), (B, D))
+    _dev(gate_row, "gate_row", (torch.bfloat16,), (B, D))
+    _check(lib().dsa_indexer_store(B, S, D, _ptr(pos), _ptr(k_row), _ptr(gate_row), _ptr(k_cache),
+                                   _ptr(gate_cache), _ptr(valid), _stream(k_cache)))
+
+
+def write_geom(seq_len, row_seq=None, row_pos=None):
+    """Decode geometry from the live lengths: (row_seq [B], row_pos [B]) int32."""
+    _dev(seq_len, "seq_len", (torch.int32,))
+    B = seq_len.shape[0]
+    if row_seq is None:
+        row_seq = torch.empty((B,), dtype=torch.int32, device=seq_len.device)
+    if row_pos is None:
+        row_pos = torch.empty((B,), dtype=torch.int32, device=seq_len.device)
+    _dev(row_seq, "row_seq", (torch.int32,), (B,))
+    _dev(row_pos, "row_pos", (torch.int32,), (B,))
+    _check(lib().dsa_write_geom(B, _ptr(seq_len), _ptr(row_seq), _ptr(row_pos), _stream(seq_len)))
+    return row_seq, row_pos
+
+
+def pool_append(cfg: Config, pos, k, gate, ape, valid, pool_keys, pool_valid, ids, n_valid, *,
+                first_key: int, pool_key_scales=None):
+    """The pool each sequence's new token (pos [B]) completes: key (bf16, or fp8 codes with
+    pool_key_scales) and validity as kpool_compress computes them, and, when valid, its id
+    appended to ids/n_valid. Everything is updated in place."""
+    _dev(k, "k", (torch.bfloat16,))
+    B, S, D = k.shape
+    KP = cfg.index_kpool
+    _dev(gate, "gate", (torch.bfloat16,), (B, S, D))
+    _dev(ape, "ape", (torch.float32,), (KP, D))
+    _dev(valid, "valid", (torch.uint8,), (B, S))
+    _dev(pos, "pos", (torch.int32,), (B,))
+    P = num_pools(S, first_key, KP)
+    if pool_key_scales is None:
+        _dev(pool_keys, "pool_keys", (torch.bfloat16,), (B, P, D))
+    else:
+        _dev(pool_keys, "pool_keys", _FP8, (B, P, D))
+        _dev(pool_key_scales, "pool_key_scales", (torch.float32,), (B, P))
+    _dev(pool_valid, "pool_valid", (torch.uint8,), (B, P))
+    _dev(ids, "ids", (torch.int32,), (B, P))
+    _dev(n_valid, "n_valid", (torch.int32,), (B,))
+    _check(lib().dsa_pool_append(ctypes.byref(cfg), B, S, first_key, _ptr(pos), _ptr(k),
+                                 _ptr(gate), _ptr(ape), _ptr(valid), _ptr(pool_keys),
+                                 _ptr(pool_key_scales), _ptr(pool_valid), _ptr(ids),
+                                 _ptr(n_valid), _stream(k)))
 
 
 def compact_pools(pool_valid, ids=None, n_valid=None):

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(HERE, "libdsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-KERNELS = ["kpool_compress.hip", "compact_pools.hip", "index_scores.hip", "topk_pools.hip",
+KERNELS = ["kpool_compress.hip", "cache_update.hip", "compact_pools.hip", "index_scores.hip",
+           "topk_pools.hip",
            "expand_selection.hip", "sparse_mla_decode.hip"]
 HOST = ["dsa_api.cpp", "absorb.cpp"]
 

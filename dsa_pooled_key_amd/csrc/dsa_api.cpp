@@ -173,6 +173,74 @@ int dsa_kpool_compress_fp8(const dsa_config *cfg, int B, int S, int first_key, c
                       "kpool_compress_fp8 launch");
 }
 
+int dsa_k_norm(int64_t rows, int D, void *x, const void *weight, const void *bias, float eps,
+               hipStream_t stream) {
+    clear_error();
+    if (rows < 0 || D <= 0) return set_error(DSA_ERR_BAD_SIZE, "k_norm: rows >= 0 and D > 0 needed");
+    if (D % 8 != 0 || D > 512 || ((D / 8) & (D / 8 - 1)) != 0)
+        return set_error(DSA_ERR_UNSUPPORTED, "k_norm: D = %d must be 8 times a power of two, at most 512", D);
+    if (!(eps >= 0.0f)) return set_error(DSA_ERR_BAD_SIZE, "k_norm: eps must be >= 0");
+    if (rows > INT32_MAX) return set_error(DSA_ERR_UNSUPPORTED, "k_norm: rows above 2^31 - 1");
+    if (rows == 0) return DSA_OK;
+    if (!x || !weight || !bias) return set_error(DSA_ERR_NULL_ARG, "k_norm: a buffer is NULL");
+    if (!aligned(x, 16) || !aligned(weight, 16) || !aligned(bias, 16))
+        return set_error(DSA_ERR_BAD_SIZE, "k_norm: x, weight and bias need 16-byte alignment");
+    return hip_status(dsa::launch_layer_norm((long long)rows, D, static_cast<uint16_t *>(x),
+                                             static_cast<const uint16_t *>(weight),
+                                             static_cast<const uint16_t *>(bias), eps, stream),
+                      "k_norm launch");
+}
+
+int dsa_indexer_store(int B, int S, int D, const int32_t *pos, const void *k_row, const void *gate_row,
+                      void *k_cache, void *gate_cache, uint8_t *valid, hipStream_t stream) {
+    clear_error();
+    if (B < 0 || S < 0 || D <= 0) return set_error(DSA_ERR_BAD_SIZE, "indexer_store: B, S >= 0 and D > 0 needed");
+    if (D % 8 != 0) return set_error(DSA_ERR_UNSUPPORTED, "indexer_store: D = %d must be a multiple of 8", D);
+    if (B == 0 || S == 0) return DSA_OK;
+    if (!pos || !k_row || !gate_row || !k_cache || !gate_cache || !valid)
+        return set_error(DSA_ERR_NULL_ARG, "indexer_store: a buffer is NULL");
+    if (!aligned(k_row, 16) || !aligned(gate_row, 16) || !aligned(k_cache, 16) || !aligned(gate_cache, 16))
+        return set_error(DSA_ERR_BAD_SIZE, "indexer_store: rows and caches need 16-byte alignment");
+    return hip_status(dsa::launch_indexer_store(B, S, D, pos, static_cast<const uint16_t *>(k_row),
+                                                static_cast<const uint16_t *>(gate_row),
+                                                static_cast<uint16_t *>(k_cache),
+                                                static_cast<uint16_t *>(gate_cache), valid, stream),
+                      "indexer_store launch");
+}
+
+int dsa_write_geom(int B, const int32_t *seq_len, int32_t *row_seq, int32_t *row_pos, hipStream_t stream) {
+    clear_error();
+    if (B < 0) return set_error(DSA_ERR_BAD_SIZE, "write_geom: negative B");
+    if (B == 0) return DSA_OK;
+    if (!seq_len || !row_seq || !row_pos) return set_error(DSA_ERR_NULL_ARG, "write_geom: a buffer is NULL");
+    return hip_status(dsa::launch_write_geom(B, seq_len, row_seq, row_pos, stream), "write_geom launch");
+}
+
+int dsa_pool_append(const dsa_config *cfg, int B, int S, int first_key, const int32_t *pos,
+                    const void *k, const void *gate, const float *ape, const uint8_t *valid,
+                    void *pool_keys, float *pool_key_scales, uint8_t *pool_valid, int32_t *ids,
+                    int32_t *n_valid, hipStream_t stream) {
+    clear_error();
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    const int D = cfg->index_head_dim;
+    if (D < 8 || D > 512 || (D & (D - 1)) != 0)
+        return set_error(DSA_ERR_UNSUPPORTED, "pool_append: index_head_dim %d must be a power of two in [8, 512]", D);
+    if (B < 0 || S < 0 || first_key < 0) return set_error(DSA_ERR_BAD_SIZE, "negative B, S or first_key");
+    const int64_t P = num_pools(S, first_key, cfg->index_kpool);
+    if ((int64_t)B * P == 0) return DSA_OK;
+    if (!pos || !k || !gate || !ape || !valid || !pool_keys || !pool_valid || !ids || !n_valid)
+        return set_error(DSA_ERR_NULL_ARG, "pool_append: a buffer is NULL");
+    if (!aligned(k, 16) || !aligned(gate, 16) || !aligned(ape, 16) ||
+        !aligned(pool_keys, pool_key_scales ? 8 : 16))
+        return set_error(DSA_ERR_BAD_SIZE, "pool_append: k, gate, ape and pool_keys need 16-byte alignment (8 for fp8 keys)");
+    return hip_status(dsa::launch_pool_append(B, S, D, cfg->index_kpool, first_key, (int)P, pos,
+                                              static_cast<const uint16_t *>(k),
+                                              static_cast<const uint16_t *>(gate), ape, valid, pool_keys,
+                                              pool_key_scales, pool_valid, ids, n_valid, stream),
+                      "pool_append launch");
+}
+
 int dsa_quantize_rows_fp8(int64_t rows, int n, const void *src, dsa_dtype src_dtype, uint8_t *codes,
                           float *scales, hipStream_t stream) {
     clear_error();

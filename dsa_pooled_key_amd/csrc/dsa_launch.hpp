@@ -15,6 +15,22 @@ hipError_t launch_kpool_compress(int B, int S, int D, int KP, int first_key, int
                                  const uint16_t *k, const uint16_t *gate, const float *ape,
                                  const uint8_t *valid, void *pool_keys, float *key_scales,
                                  uint8_t *pool_valid, hipStream_t stream);
+// The pool each sequence's new token completes (key_scales NULL: bf16 keys, else fp8), and
+// its id appended to the compacted list when valid.
+hipError_t launch_pool_append(int B, int S, int D, int KP, int first_key, int P,
+                              const int32_t *pos, const uint16_t *k, const uint16_t *gate,
+                              const float *ape, const uint8_t *valid, void *pool_keys,
+                              float *key_scales, uint8_t *pool_valid, int32_t *ids,
+                              int32_t *n_valid, hipStream_t stream);
+// LayerNorm with a bias over bf16 rows of D, in place (D/8 a power of two up to 64).
+hipError_t launch_layer_norm(long long rows, int D, uint16_t *x, const uint16_t *weight,
+                             const uint16_t *bias, float eps, hipStream_t stream);
+// Staged rows to their positions, marked valid; decode geometry from the live lengths.
+hipError_t launch_indexer_store(int B, int S, int D, const int32_t *pos, const uint16_t *k_row,
+                                const uint16_t *gate_row, uint16_t *k_cache, uint16_t *gate_cache,
+                                uint8_t *valid, hipStream_t stream);
+hipError_t launch_write_geom(int B, const int32_t *seq_len, int32_t *row_seq, int32_t *row_pos,
+                             hipStream_t stream);
 // Rows of n values (bf16 or f32) -> e4m3 codes and per-row f32 scales.
 hipError_t launch_quantize_rows(long long rows, int n, const void *src, bool f32_src,
                                 uint8_t *codes, float *scales, hipStream_t stream);

@@ -34,25 +34,15 @@ __device__ __forceinline__ float fp8_row_scale(float amax) {
     return amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
 }
 
-// FP8OUT: the pooled key is rounded to bf16 as usual and then stored as fp8, quantized per
-// pool row: scale s = amax/448 over the row's D values (the row's D/8 threads are
-// consecutive lanes and meet through lane swaps), codes e4m3(value / s).
-template <int KP, bool FP8OUT = false>
-__global__ __launch_bounds__(256) void kpool_compress_kernel(
-    int S, int D, int first_key, int P, long long n_pools, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ gate, const float *__restrict__ ape,
-    const uint8_t *__restrict__ valid, void *__restrict__ pool_keys,
-    float *__restrict__ key_scales, uint8_t *__restrict__ pool_valid) {
-    const int tpp = D >> 3;  // threads per pool
-    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long long pool = gid / tpp;
-    if (pool >= n_pools) return;
-    const int d0 = (int)(gid - pool * tpp) * 8;
-    const long long b = pool / P;
-    const long long p = pool - b * P;
-    const long long t0 = (long long)first_key + p * KP;
-    const long long row0 = b * S + t0;
-
+// Channels d0 .. d0+7 of pool p of sequence b: the softmax over the KP slots of gate + ape
+// weighting the slot keys, rounded to bf16 (four packed pairs).
+template <int KP>
+__device__ __forceinline__ u32x4 pool_channels8(int S, int D, int first_key, long long b,
+                                                long long p, int d0,
+                                                const uint16_t *__restrict__ k,
+                                                const uint16_t *__restrict__ gate,
+                                                const float *__restrict__ ape) {
+    const long long row0 = b * S + (long long)first_key + p * KP;
     float x[KP][8];
     float mx[8];
 #pragma unroll
@@ -94,6 +84,16 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
     o.y = pack_bf16x2(acc[2] / den[2], acc[3] / den[3]);
     o.z = pack_bf16x2(acc[4] / den[4], acc[5] / den[5]);
     o.w = pack_bf16x2(acc[6] / den[6], acc[7] / den[7]);
+    return o;
+}
+
+// Stores channels d0 .. d0+7 of pool row `pool` (index into [B*P]): bf16, or (FP8OUT) fp8
+// quantized per pool row -- scale s = amax/448 over the row's D values, whose D/8 threads
+// are consecutive lanes (tpp of them, a power of two) and meet through lane swaps.
+template <bool FP8OUT>
+__device__ __forceinline__ void store_pool_channels8(const u32x4 &o, long long pool, int D, int d0,
+                                                     int tpp, void *__restrict__ pool_keys,
+                                                     float *__restrict__ key_scales) {
     if constexpr (!FP8OUT) {
         *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(pool_keys) + pool * D + d0) = o;
     } else {
@@ -114,11 +114,68 @@ __global__ __launch_bounds__(256) void kpool_compress_kernel(
             u32x2{e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7])};
         if (d0 == 0) key_scales[pool] = sc;
     }
+}
+
+// FP8OUT: the pooled key is rounded to bf16 as usual and then stored as fp8 (see above).
+template <int KP, bool FP8OUT = false>
+__global__ __launch_bounds__(256) void kpool_compress_kernel(
+    int S, int D, int first_key, int P, long long n_pools, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ gate, const float *__restrict__ ape,
+    const uint8_t *__restrict__ valid, void *__restrict__ pool_keys,
+    float *__restrict__ key_scales, uint8_t *__restrict__ pool_valid) {
+    const int tpp = D >> 3;  // threads per pool
+    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long pool = gid / tpp;
+    if (pool >= n_pools) return;  // whole groups of tpp lanes
+    const int d0 = (int)(gid - pool * tpp) * 8;
+    const long long b = pool / P;
+    const long long p = pool - b * P;
+    const u32x4 o = pool_channels8<KP>(S, D, first_key, b, p, d0, k, gate, ape);
+    store_pool_channels8<FP8OUT>(o, pool, D, d0, tpp, pool_keys, key_scales);
     if (d0 == 0) {
+        const long long row0 = b * S + (long long)first_key + p * KP;
         int ok = 1;
 #pragma unroll
         for (int s = 0; s < KP; ++s) ok &= valid[row0 + s] != 0;
         pool_valid[pool] = (uint8_t)ok;
+    }
+}
+
+// Decode-time upkeep: block b (one wave) looks at the token just stored at pos[b]; when it
+// is the last slot of pool p (pos >= first_key, (pos - first_key + 1) % KP == 0, p < P), the
+// wave computes that pool exactly as kpool_compress_kernel does (lanes < D/8, 8 channels
+// each), sets its validity and, if valid, appends p to the compacted ids unless the list
+// already ends at p or beyond (so a repeated call changes nothing).
+template <int KP, bool FP8OUT>
+__global__ __launch_bounds__(64) void pool_append_kernel(
+    int S, int D, int first_key, int P, const int32_t *__restrict__ pos,
+    const uint16_t *__restrict__ k, const uint16_t *__restrict__ gate,
+    const float *__restrict__ ape, const uint8_t *__restrict__ valid,
+    void *__restrict__ pool_keys, float *__restrict__ key_scales,
+    uint8_t *__restrict__ pool_valid, int32_t *__restrict__ ids, int32_t *__restrict__ n_valid) {
+    const long long b = blockIdx.x;
+    const int t = pos[b];
+    if (t < first_key || t >= S || (t - first_key + 1) % KP != 0) return;
+    const long long p = (t - first_key + 1) / KP - 1;
+    if (p >= P) return;
+    const int tpp = D >> 3;
+    const int lane = threadIdx.x;
+    if (lane < tpp) {
+        const int d0 = lane * 8;
+        const u32x4 o = pool_channels8<KP>(S, D, first_key, b, p, d0, k, gate, ape);
+        store_pool_channels8<FP8OUT>(o, b * P + p, D, d0, tpp, pool_keys, key_scales);
+    }
+    if (lane == 0) {
+        const long long row0 = b * S + (long long)first_key + p * KP;
+        int ok = 1;
+#pragma unroll
+        for (int s = 0; s < KP; ++s) ok &= valid[row0 + s] != 0;
+        pool_valid[b * P + p] = (uint8_t)ok;
+        const int n = n_valid[b];
+        if (ok && n >= 0 && n < P && (n == 0 || ids[b * P + n - 1] < p)) {
+            ids[b * P + n] = (int32_t)p;
+            n_valid[b] = n + 1;
+        }
     }
 }
 
@@ -240,6 +297,30 @@ hipError_t launch_kpool_compress(int B, int S, int D, int KP, int first_key, int
 #undef DSA_KP_CASE
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_pool_append(int B, int S, int D, int KP, int first_key, int P,
+                              const int32_t *pos, const uint16_t *k, const uint16_t *gate,
+                              const float *ape, const uint8_t *valid, void *pool_keys,
+                              float *key_scales, uint8_t *pool_valid, int32_t *ids,
+                              int32_t *n_valid, hipStream_t stream) {
+    if (B == 0 || P == 0) return hipSuccess;
+#define DSA_APPEND(n, f8)                                                                        \
+    hipLaunchKernelGGL((pool_append_kernel<n, f8>), dim3(B), dim3(64), 0, stream, S, D, first_key, P, \
+                       pos, k, gate, ape, valid, pool_keys, key_scales, pool_valid, ids, n_valid)
+#define DSA_APPEND_KP(n)                              \
+    case n:                                           \
+        if (key_scales) DSA_APPEND(n, true);          \
+        else DSA_APPEND(n, false);                    \
+        break;
+    switch (KP) {
+        DSA_APPEND_KP(1) DSA_APPEND_KP(2) DSA_APPEND_KP(3) DSA_APPEND_KP(4)
+        DSA_APPEND_KP(5) DSA_APPEND_KP(6) DSA_APPEND_KP(7) DSA_APPEND_KP(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef DSA_APPEND_KP
+#undef DSA_APPEND
+    return hipGetLastError();
 }
 
 hipError_t launch_quantize_rows(long long rows, int n, const void *src, bool f32_src,

@@ -151,6 +151,46 @@ int dsa_kpool_compress_fp8(const dsa_config *cfg, int B, int S, int first_key, c
 int dsa_quantize_rows_fp8(int64_t rows, int n, const void *src, dsa_dtype src_dtype, uint8_t *codes,
                           float *scales, hipStream_t stream);
 
+/* ------------------------------------------------------------------ decode-time upkeep */
+/* The per-step maintenance of the indexer cache that comes before the selection chain in a
+ * decode step (one new token per sequence). The pages name these kernels in mod.rs,
+ * Glm5NextDsaKernels.
+ *
+ * k_norm: indexer.k_norm is a LayerNorm with a bias (not an RMSNorm), applied in place:
+ * per row of D values, y = (x - mean) / sqrt(var + eps) * weight + bias with the biased
+ * variance, f32 arithmetic, bf16 out. x: [rows, D] bf16 (in place, 16-byte aligned);
+ * weight, bias: [D] bf16. D must be 8 times a power of two, at most 512. */
+int dsa_k_norm(int64_t rows, int D, void *x, const void *weight, const void *bias, float eps,
+               hipStream_t stream);
+
+/* indexer_store: copies each sequence's staged indexer row -- the new token's (normalized)
+ * key and its gate values -- to the device-side position pos[b] and marks that slot valid.
+ * A position outside [0, S) stores nothing. pos: [B] i32 (device); k_row, gate_row: [B, D]
+ * bf16; k_cache, gate_cache: [B, S, D] bf16; valid: [B, S] u8. D a multiple of 8. */
+int dsa_indexer_store(int B, int S, int D, const int32_t *pos, const void *k_row, const void *gate_row,
+                      void *k_cache, void *gate_cache, uint8_t *valid, hipStream_t stream);
+
+/* write_geom: the selector geometry from the live lengths, on the device (so a captured graph
+ * replays over the live context): one decode row per sequence, row_seq[b] = b and
+ * row_pos[b] = seq_len[b] - 1. seq_len, row_seq, row_pos: [B] i32. */
+int dsa_write_geom(int B, const int32_t *seq_len, int32_t *row_seq, int32_t *row_pos, hipStream_t stream);
+
+/* pool_append: the pool that the token at pos[b] completes (mod.rs, "Checkpoint and kernel
+ * facts": pooling starts at first_key; a pool counts only when all its slots are valid). When
+ * pos >= first_key, (pos - first_key + 1) % KP == 0 and p = (pos - first_key + 1)/KP - 1 < P,
+ * pool p's key and validity are computed exactly as dsa_kpool_compress (bf16 keys,
+ * pool_key_scales NULL) or dsa_kpool_compress_fp8 (fp8 codes, pool_key_scales [B, P]) computes
+ * them, and a valid p is appended to the compacted list of dsa_compact_pools
+ * (ids[b, n_valid[b]] = p, n_valid[b] += 1) unless the list already ends at p or beyond, so
+ * a repeated call changes nothing. Other positions change nothing. Storing every token this
+ * way keeps pool_keys, pool_valid, ids and n_valid equal to the batch calls. Arguments as
+ * dsa_kpool_compress and dsa_compact_pools; pos: [B] i32 (device). D a power of two in
+ * [8, 512]. */
+int dsa_pool_append(const dsa_config *cfg, int B, int S, int first_key, const int32_t *pos,
+                    const void *k, const void *gate, const float *ape, const uint8_t *valid,
+                    void *pool_keys, float *pool_key_scales, uint8_t *pool_valid, int32_t *ids,
+                    int32_t *n_valid, hipStream_t stream);
+
 /* ------------------------------------------------------------------ step 2 */
 /* mod.rs names dsa_compact_pools between pooling and scoring. Stable compaction per
  * sequence: ids[b, 0..n_valid[b]) are the valid pool indices in ascending order, the rest of

@@ -527,6 +527,153 @@ def test_quantize_rows_fp8_bit_exact(n):
                                    src[tuple(bad[0])] / rs[bad[0][0]])
 
 
+# ------------------------------------------------------------------ decode-time upkeep
+
+def _bf(a):
+    return _dev(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_k_norm(D):
+    """LayerNorm with a bias, in place: within one bf16 ulp of the oracle (f32 against
+    double arithmetic); bit-exact on rows whose mean, variance and square root are exact
+    (halves at c + a and c - a, a a power of two, eps 0)."""
+    rng = np.random.default_rng(D)
+    rows = 777
+    x = synth.bf16_bits((rng.standard_normal((rows, D)) * rng.uniform(0.1, 4, (rows, 1))
+                         + rng.standard_normal((rows, 1)) * 3).astype(np.float32))
+    w = synth.bf16_bits((1 + 0.3 * rng.standard_normal(D)).astype(np.float32))
+    b = synth.bf16_bits((0.2 * rng.standard_normal(D)).astype(np.float32))
+    xt = _bf(x)
+    dsa.k_norm(xt, _bf(w), _bf(b), 1e-5)
+    ref = synth.bf16_to_f32(oracle.layer_norm(x, w, b, 1e-5)).astype(np.float64)
+    got = synth.bf16_to_f32(_bits(xt)).astype(np.float64)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+    bad = np.abs(got - ref) > ulp + 1e-7
+    assert not bad.any(), (np.argwhere(bad)[:4], got[bad][:4], ref[bad][:4])
+    # exact rows
+    a = np.exp2(rng.integers(-3, 4, (64, 1)))
+    c = rng.integers(-16, 17, (64, 1)) / 4.0
+    sign = np.where(rng.permuted(np.tile(np.arange(D) % 2, (64, 1)), axis=1) == 0, -1.0, 1.0)
+    xe = synth.bf16_bits((c + a * sign).astype(np.float32))
+    we = synth.bf16_bits((rng.integers(-8, 9, D) / 4.0).astype(np.float32))
+    be = synth.bf16_bits((rng.integers(-8, 9, D) / 8.0).astype(np.float32))
+    xt = _bf(xe)
+    dsa.k_norm(xt, _bf(we), _bf(be), 0.0)
+    assert np.array_equal(_bits(xt), oracle.layer_norm(xe, we, be, 0.0))
+
+
+def test_indexer_store_and_write_geom():
+    rng = np.random.default_rng(60)
+    B, S, D = 6, 50, 128
+    kc = rng.integers(0, 65535, (B, S, D)).astype(np.uint16) & 0x7f7f
+    gc = rng.integers(0, 65535, (B, S, D)).astype(np.uint16) & 0x7f7f
+    valid = (rng.random((B, S)) > 0.5).astype(np.uint8)
+    kr = rng.integers(0, 65535, (B, D)).astype(np.uint16) & 0x7f7f
+    gr = rng.integers(0, 65535, (B, D)).astype(np.uint16) & 0x7f7f
+    pos = np.array([0, 49, 50, -1, 17, 17], np.int32)
+    tk, tg, tv = _bf(kc), _bf(gc), _dev(valid)
+    dsa.indexer_store(_dev(pos), _bf(kr), _bf(gr), tk, tg, tv)
+    rk, rg, rv = oracle.indexer_store(pos, kr, gr, kc, gc, valid)
+    assert np.array_equal(_bits(tk), rk) and np.array_equal(_bits(tg), rg)
+    assert np.array_equal(tv.cpu().numpy(), rv)
+    lens = np.array([1, 131072, 4096, 0, 77, 5000], np.int32)
+    rs, rp = dsa.write_geom(_dev(lens))
+    ors, orp = oracle.write_geom(lens)
+    assert np.array_equal(rs.cpu().numpy(), ors) and np.array_equal(rp.cpu().numpy(), orp)
+
+
+@pytest.mark.parametrize("kp,f,fp8", [(4, 0, False), (8, 5, True), (3, 2, False), (8, 0, True)])
+def test_pool_append_token_by_token_equals_batch(kp, f, fp8):
+    """A cache filled one token per step (indexer_store, then pool_append) ends with the pool
+    keys, validity and compacted ids of the batch calls (the GPU's own batch pooling, bit for
+    bit; the oracle's compaction, bit for bit; the oracle's keys within one bf16 ulp); a
+    repeated append changes nothing."""
+    rng = np.random.default_rng(61 + kp)
+    B, S, D = 3, 70, 128
+    cfg = dsa.Config.make(index_heads=32, index_head_dim=D, index_kpool=kp, index_topk=8 * kp,
+                          heads=32)
+    k = synth.bf16_bits(rng.standard_normal((B, S, D)).astype(np.float32))
+    gate = synth.bf16_bits(rng.standard_normal((B, S, D)).astype(np.float32))
+    ape = rng.standard_normal((kp, D)).astype(np.float32)
+    fv = (rng.random((B, S)) > 0.08).astype(np.uint8)
+    P = oracle.num_pools(S, f, kp)
+    kc = torch.zeros((B, S, D), dtype=torch.bfloat16, device="cuda")
+    gc = torch.zeros_like(kc)
+    vc = torch.zeros((B, S), dtype=torch.uint8, device="cuda")
+    pk = torch.zeros((B, P, D), dtype=torch.uint8 if fp8 else torch.bfloat16, device="cuda")
+    sc = torch.zeros((B, P), dtype=torch.float32, device="cuda") if fp8 else None
+    pv = torch.zeros((B, P), dtype=torch.uint8, device="cuda")
+    ids = torch.full((B, P), -1, dtype=torch.int32, device="cuda")
+    nv = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    ta, kt, gt, fvt = _dev(ape), _bf(k), _bf(gate), _dev(fv)
+    for t in range(S):
+        pos = torch.full((B,), t, dtype=torch.int32, device="cuda")
+        dsa.indexer_store(pos, kt[:, t].contiguous(), gt[:, t].contiguous(), kc, gc, vc)
+        vc[:, t] = fvt[:, t]
+        for _ in range(2):
+            dsa.pool_append(cfg, pos, kc, gc, ta, vc, pk, pv, ids, nv, first_key=f,
+                            pool_key_scales=sc)
+    torch.cuda.synchronize()
+    if fp8:
+        bk, bsc, bpv = dsa.kpool_compress_fp8(cfg, kt, gt, ta, fvt, f)
+        assert torch.equal(sc, bsc)
+    else:
+        bk, bpv = dsa.kpool_compress(cfg, kt, gt, ta, fvt, f)
+    assert torch.equal(pk.view(torch.uint8), bk.view(torch.uint8)) and torch.equal(pv, bpv)
+    rk, rv = oracle.kpool_compress(k, gate, ape, fv, kp, f)
+    rids, rnv = oracle.compact_pools(rv)
+    assert np.array_equal(pv.cpu().numpy(), rv)
+    assert np.array_equal(ids.cpu().numpy(), rids) and np.array_equal(nv.cpu().numpy(), rnv)
+    if not fp8:
+        a = synth.bf16_to_f32(_bits(pk)).astype(np.float64)
+        r = synth.bf16_to_f32(rk).astype(np.float64)
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -126))) - 7)
+        assert np.all(np.abs(a - r) <= ulp + 1e-6)
+
+
+@pytest.mark.parametrize("name", ["ragged_fp8", "ragged_bf16", "decode_b8_32k"])
+def test_pool_append_one_decode_step_against_the_oracle(name):
+    """One decode step on a workload's token cache, each sequence at its own position (some
+    completing a pool, one inside a pool, one past the cache): keys, validity and ids as the
+    oracle's append of the same step."""
+    ki = synth.make_kpool_inputs(name, batch=KPOOL_BATCH.get(name))
+    wl = ki.wl
+    cfg = config_for(wl)
+    B, S, D = ki.k.shape
+    f, kp = wl.first_key, wl.kpool
+    rng = np.random.default_rng(62)
+    pos = rng.integers(f + kp, S, B).astype(np.int32)
+    pos = f + ((pos - f) // kp) * kp + kp - 1                      # each completes a pool
+    pos[-1] = S + 3
+    if B > 2:
+        pos[-2] -= 1                                               # inside a pool
+    rk, rv = oracle.kpool_compress(ki.k, ki.gate, ki.ape, ki.valid, kp, f)
+    before = rv.copy()
+    done = [b for b in range(B) if 0 <= pos[b] < S and (pos[b] - f + 1) % kp == 0]
+    for b in done:       # the pool this step completes is not there yet
+        before[b, (pos[b] - f + 1) // kp - 1:] = 0
+    ids0, nv0 = oracle.compact_pools(before)
+    keys0 = np.zeros_like(rk)
+    ok_k, ok_v, ok_ids, ok_nv = oracle.pool_append(pos, ki.k, ki.gate, ki.ape, ki.valid, keys0,
+                                                   before, ids0, nv0, kpool=kp, first_key=f)
+    gk, pv, ids, nv = _bf(keys0), _dev(before), _dev(ids0), _dev(nv0)
+    dsa.pool_append(cfg, _dev(pos), _bf(ki.k), _bf(ki.gate), _dev(ki.ape), _dev(ki.valid), gk, pv,
+                    ids, nv, first_key=f)
+    assert np.array_equal(pv.cpu().numpy(), ok_v)
+    assert np.array_equal(ids.cpu().numpy(), ok_ids) and np.array_equal(nv.cpu().numpy(), ok_nv)
+    a = synth.bf16_to_f32(_bits(gk)).astype(np.float64)
+    r = synth.bf16_to_f32(ok_k).astype(np.float64)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 2.0 ** -126))) - 7)
+    assert np.all(np.abs(a - r) <= ulp + 1e-6)
+    assert len(done) >= 1 and (nv.cpu().numpy() - nv0).sum() == sum(
+        int(rv[b, (pos[b] - f + 1) // kp - 1]) for b in done)
+
+
 # ------------------------------------------------------------------ chains
 
 def _oracle_select(di, ids, nv, rows):
