@@ -68,6 +68,11 @@ def lib():
         L.orc_sparse_mla.argtypes = [_I, _I, _I, _I, _D, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I,
                                      _P, _P]
         L.orc_sparse_mla.restype = None
+        L.orc_topk_to_mask.argtypes = [_I, _I, _I, _P, _P]
+        L.orc_topk_to_mask.restype = None
+        L.orc_masked_attn.argtypes = [_I, _I, _I, _I, _D, _P, _P, _P, _P, _I, _P, _P, _I, _I, _P,
+                                      _P]
+        L.orc_masked_attn.restype = None
         L.orc_layer_norm.argtypes = [_L, _I, _P, _P, _P, _D]
         L.orc_layer_norm.restype = None
         L.orc_indexer_store.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P, _P]
@@ -351,6 +356,58 @@ def sparse_mla(q_abs, token_ids, row_seq, kv, *, sm_scale: float, S: int = 0, kv
     lib().orc_sparse_mla(Q, H, C, W, float(sm_scale), _ptr(q_abs), _ptr(token_ids),
                          _ptr(row_seq), _ptr(kv), int(fp8), _ptr(kv_scales) if fp8 else None,
                          int(S), _ptr(block_table), max_blocks, block_size, _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def topk_to_mask(token_ids, S: int):
+    """[Q, W] token ids -> [Q, S] u8 mask of the tokens present."""
+    token_ids = _arr(token_ids, np.int32, name="token_ids")
+    Q, W = token_ids.shape
+    mask = np.zeros((Q, S), np.uint8)
+    lib().orc_topk_to_mask(Q, W, S, _ptr(token_ids), _ptr(mask))
+    return mask
+
+
+def masked_attn(q_abs, mask, row_seq, kv, *, sm_scale: float, kv_scales=None, block_table=None,
+                block_size: int = 64):
+    """Dense attention over every masked token of each row: q_abs [Q,H,C] bf16 bits; mask
+    [Q,S] u8; kv as sparse_mla (contiguous rows b*S + t, or paged). Returns (out, lse)."""
+    q_abs = _arr(q_abs, np.uint16, name="q_abs")
+    Q, H, C = q_abs.shape
+    mask = _arr(mask, np.uint8, name="mask")
+    S = mask.shape[1]
+    row_seq = _arr(row_seq, np.int32, (Q,), "row_seq")
+    kv = np.ascontiguousarray(kv)
+    fp8 = kv.dtype == np.uint8
+    if not fp8:
+        kv = _arr(kv, np.uint16, name="kv")
+    kv = kv.reshape(-1, C)
+    rows = kv.shape[0]
+    if fp8:
+        kv_scales = _arr(kv_scales, np.float32, name="kv_scales").reshape(-1)
+    max_blocks = 0
+    if block_table is not None:
+        block_table = _arr(block_table, np.int32, name="block_table")
+        max_blocks = block_table.shape[1]
+    for r in range(Q):  # the oracle trusts its inputs: check every address first
+        t = np.nonzero(mask[r])[0]
+        if t.size == 0:
+            continue
+        b = int(row_seq[r])
+        if block_table is not None:
+            blk = t // block_size
+            ok = blk < max_blocks
+            ent = np.where(ok, block_table[b][np.minimum(blk, max_blocks - 1)], -1)
+            phys = np.where(ent >= 0, ent.astype(np.int64) * block_size + t % block_size, 0)
+        else:
+            phys = b * S + t
+        if phys.max() >= rows:
+            raise ValueError(f"row {r}: latent address out of range")
+    out = np.zeros((Q, H, C), np.float32)
+    lse = np.zeros((Q, H), np.float32)
+    lib().orc_masked_attn(Q, H, C, S, float(sm_scale), _ptr(q_abs), _ptr(mask), _ptr(row_seq),
+                          _ptr(kv), int(fp8), _ptr(kv_scales) if fp8 else None,
+                          _ptr(block_table), max_blocks, block_size, _ptr(out), _ptr(lse))
     return out, lse
 
 

@@ -434,6 +434,90 @@ void orc_sparse_mla(int Q, int H, int C, int W, double sm, const uint16_t *q_abs
     }
 }
 
+/* ---------------------------------------------------------------- dense masked cross-check */
+
+/* mod.rs, Glm5NextDsaKernels::topk_to_mask and MASKED_ATTN_MAX_KEYS (the selection turned into
+ * a token mask that a dense masked attention takes, as a second check of the sparse decode).
+ * Reading: mask[r, t] = 1 when some slot of token_ids[r] holds t (0 <= t < S), else 0.
+ * Layouts: token_ids [Q, W] i32; mask [Q, S] u8. */
+void orc_topk_to_mask(int Q, int W, int S, const int32_t *token_ids, uint8_t *mask) {
+    for (long r = 0; r < Q; ++r) {
+        for (long t = 0; t < S; ++t) mask[r * S + t] = 0;
+        for (long i = 0; i < W; ++i) {
+            long t = token_ids[r * W + i];
+            if (t >= 0 && t < S) mask[r * S + t] = 1;
+        }
+    }
+}
+
+/* mod.rs, mla_masked_attn: attention of row r, head h over every token t < S of sequence
+ * b = row_seq[r] with mask[r, t] = 1, the whole [S] score row at once: logit_t =
+ * sm * q_abs[r,h,:] . v_t, out = sum_t softmax(logit)_t v_t, lse = log sum exp(logit), with
+ * latent rows addressed as orc_sparse_mla addresses them (a token whose row is absent from
+ * the table is skipped). A row with no token: out = 0, lse = -inf.
+ * Layouts: q_abs [Q,H,C] bf16; mask [Q,S] u8; kv [rows, C] bf16 or e4m3 (+ kv_scales [rows]);
+ * out [Q,H,C] f32; lse [Q,H] f32. */
+void orc_masked_attn(int Q, int H, int C, int S, double sm, const uint16_t *q_abs,
+                     const uint8_t *mask, const int32_t *row_seq, const void *kv, int kv_fp8,
+                     const float *kv_scales, const int32_t *block_table, int max_blocks,
+                     int block_size, float *out, float *lse) {
+    long r;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < Q; ++r) {
+        long b = row_seq[r];
+        double *logit = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+        long *rows = (long *)malloc(sizeof(long) * (size_t)(S > 0 ? S : 1));
+        double *v = (double *)malloc(sizeof(double) * (size_t)C);
+        for (long t = 0; t < S; ++t) {
+            rows[t] = -1;
+            if (!mask[r * S + t]) continue;
+            if (block_table) {
+                long blk = t / block_size;
+                if (blk < max_blocks && block_table[b * max_blocks + blk] >= 0)
+                    rows[t] = (long)block_table[b * max_blocks + blk] * block_size + t % block_size;
+            } else {
+                rows[t] = b * (long)S + t;
+            }
+        }
+        for (long h = 0; h < H; ++h) {
+            const uint16_t *qh = q_abs + (r * H + h) * C;
+            double mx = -INFINITY, den = 0.0;
+            long n = 0;
+            for (long t = 0; t < S; ++t) {
+                if (rows[t] < 0) continue;
+                double dot = 0.0;
+                for (long c = 0; c < C; ++c) {
+                    double vc = kv_fp8 ? e4m3_value(((const uint8_t *)kv)[rows[t] * C + c]) *
+                                             (double)kv_scales[rows[t]]
+                                       : bf16_value(((const uint16_t *)kv)[rows[t] * C + c]);
+                    dot += bf16_value(qh[c]) * vc;
+                }
+                logit[t] = sm * dot;
+                if (logit[t] > mx) mx = logit[t];
+                ++n;
+            }
+            for (long t = 0; t < S; ++t)
+                if (rows[t] >= 0) den += exp(logit[t] - mx);
+            for (long c = 0; c < C; ++c) v[c] = 0.0;
+            for (long t = 0; t < S; ++t) {
+                if (rows[t] < 0) continue;
+                double pw = exp(logit[t] - mx) / den;
+                for (long c = 0; c < C; ++c) {
+                    double vc = kv_fp8 ? e4m3_value(((const uint8_t *)kv)[rows[t] * C + c]) *
+                                             (double)kv_scales[rows[t]]
+                                       : bf16_value(((const uint16_t *)kv)[rows[t] * C + c]);
+                    v[c] += pw * vc;
+                }
+            }
+            for (long c = 0; c < C; ++c) out[(r * H + h) * C + c] = n ? (float)v[c] : 0.0f;
+            if (lse) lse[r * H + h] = n ? (float)(mx + log(den)) : -INFINITY;
+        }
+        free(logit);
+        free(rows);
+        free(v);
+    }
+}
+
 /* ---------------------------------------------------------------- decode-time cache maintenance */
 
 /* mod.rs, Glm5NextDsaKernels::k_norm: indexer.k_norm is a LayerNorm with a bias (not an

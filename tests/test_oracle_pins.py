@@ -845,3 +845,61 @@ def test_pool_append_token_by_token_equals_the_batch_pooling(kp, f):
     rids, rnv = oracle.compact_pools(rv)
     assert np.array_equal(pv, rv) and np.array_equal(pk, rk)
     assert np.array_equal(ids, rids) and np.array_equal(nv, rnv)
+
+
+# ------------------------------------------------------------------ dense masked cross-check
+
+def test_topk_to_mask_by_enumeration():
+    tok = np.array([[3, -1, 7, 7, 12, 40], [-1, -1, -1, -1, -1, -1], [0, 1, 2, 39, -5, 99]],
+                   np.int32)
+    m = oracle.topk_to_mask(tok, 40)
+    for r in range(3):
+        want = {int(t) for t in tok[r] if 0 <= t < 40}
+        assert set(np.nonzero(m[r])[0].tolist()) == want
+    assert m.dtype == np.uint8 and m.max() <= 1
+
+
+def test_masked_attn_all_ones_is_sdpa_and_mask_of_a_selection_is_the_sparse_decode():
+    """With every token masked in, the masked attention is torch's scaled dot-product
+    attention in float64; with the mask of a selection it is the sparse decode over those
+    tokens (pinned above against the same library routine), paged or not, bf16 or fp8."""
+    rng = np.random.default_rng(70)
+    Q, H, C, B, S = 3, 4, 64, 2, 48
+    q = synth.bf16_bits(rng.standard_normal((Q, H, C)).astype(np.float32) * 0.5)
+    kv = synth.bf16_bits(rng.standard_normal((B * S, C)).astype(np.float32) * 0.5)
+    seq = np.array([0, 1, 1], np.int32)
+    out, lse = oracle.masked_attn(q, np.ones((Q, S), np.uint8), seq, kv, sm_scale=0.0625)
+    qt = torch.from_numpy(synth.bf16_to_f32(q).astype(np.float64))
+    kt = torch.from_numpy(synth.bf16_to_f32(kv).astype(np.float64)).reshape(B, S, C)
+    for r in range(Q):
+        k = kt[seq[r]]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt[r][None], k[None].expand(1, -1, -1), k[None], scale=0.0625)[0]
+        assert np.allclose(out[r], ref.numpy(), rtol=1e-6, atol=1e-7)
+        lref = torch.logsumexp(0.0625 * qt[r] @ k.T, dim=-1).numpy()
+        assert np.allclose(lse[r], lref, rtol=1e-6, atol=1e-6)
+    tok = np.full((Q, 20), -1, np.int32)
+    for r in range(Q):
+        tok[r, :15] = np.sort(rng.choice(S, 15, replace=False))
+    tok[2] = -1
+    mask = oracle.topk_to_mask(tok, S)
+    a, la = oracle.masked_attn(q, mask, seq, kv, sm_scale=0.0625)
+    b, lb = oracle.sparse_mla(q, tok, seq, kv, sm_scale=0.0625, S=S)
+    assert np.allclose(a, b, rtol=1e-6, atol=1e-7) and np.allclose(la[:2], lb[:2], rtol=1e-6)
+    assert np.all(a[2] == 0) and np.all(np.isneginf(la[2]))
+    # paged and fp8
+    bs = 16
+    table = rng.permutation(B * S // bs).astype(np.int32).reshape(B, S // bs)
+    codes, sc = synth.e4m3_quantize_rows(synth.bf16_to_f32(kv))
+    paged_c = np.zeros_like(codes)
+    paged_s = np.zeros_like(sc)
+    for bb in range(B):
+        for j in range(S // bs):
+            src = slice(bb * S + j * bs, bb * S + (j + 1) * bs)
+            dst = slice(table[bb, j] * bs, (table[bb, j] + 1) * bs)
+            paged_c[dst], paged_s[dst] = codes[src], sc[src]
+    c, lc = oracle.masked_attn(q, mask, seq, paged_c, sm_scale=0.0625, kv_scales=paged_s,
+                               block_table=table, block_size=bs)
+    d, ld = oracle.sparse_mla(q, tok, seq, paged_c, sm_scale=0.0625, kv_scales=paged_s,
+                              block_table=table, block_size=bs)
+    assert np.allclose(c, d, rtol=1e-6, atol=1e-7) and np.allclose(lc[:2], ld[:2], rtol=1e-6)
