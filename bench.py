@@ -170,9 +170,59 @@ def run_chain(name, steps, warmup, seed=0, replicas=0):
     return out
 
 
+def masked_check_line(args):
+    """The dense masked-attention cross-check (topk_to_mask + mla_masked_attn) on the 32K
+    decode workload's selection: microseconds per launch from graphs of several launches."""
+    import torch
+
+    from dsa_pooled_key_amd import binding as dsa
+    from dsa_pooled_key_amd import synth
+    from dsa_pooled_key_amd.pipeline import DecodeStep, DeviceDecodeInputs
+
+    di = synth.make_decode_inputs("decode_b8_32k", seed=args.seed)
+    wl = di.wl
+    x = DeviceDecodeInputs.upload(di, torch.device("cuda:0"))
+    st = DecodeStep(wl, x, di.scale, di.sm_scale)
+    st.run()
+    mask = dsa.topk_to_mask(st.token_ids, wl.S)
+    out = torch.empty_like(st.out)
+    lse = torch.empty_like(st.lse)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    fns = {"topk_to_mask": lambda: dsa.topk_to_mask(st.token_ids, wl.S, mask),
+           "mla_masked_attn": lambda: dsa.mla_masked_attn(
+               st.cfg, x.q_abs, mask, x.row_seq, x.kv, B=wl.B, sm_scale=di.sm_scale, out=out,
+               lse=lse),
+           "sparse_mla_decode": st.attend}
+    res = {}
+    for nm, fn in fns.items():
+        fn()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(4):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(5):
+            g.replay()
+        b.record(stream)
+        b.synchronize()
+        res[nm] = round(a.elapsed_time(b) / 20 * 1e3, 2)
+    torch.cuda.set_stream(torch.cuda.default_stream())
+    n_tok = int((st.token_ids >= 0).sum().item())
+    return {"workload": f"{wl.name}: {wl.Q} rows, {wl.heads} heads, every masked token of an "
+                        f"{wl.S}-position score row ({n_tok} tokens selected in all)",
+            "launch_us": res}
+
+
 def extra_lines(args):
     """X128 decode and C4 prefill, reported beside the main line."""
     extra = {}
+    if not args.no_masked:
+        extra["masked_check"] = masked_check_line(args)
     if not args.no_x128:
         r = run_chain("decode_b8_128k", args.extra_steps, args.warmup, args.seed)
         wl = r["di"].wl
@@ -463,6 +513,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-x128", action="store_true", help="skip the X128 decode line")
     ap.add_argument("--no-prefill", action="store_true", help="skip the C4 prefill line")
+    ap.add_argument("--no-masked", action="store_true",
+                    help="skip the dense masked-attention cross-check line")
     ap.add_argument("--extra-steps", type=int, default=60,
                     help="timed steps of the X128 and prefill lines")
     ap.add_argument("--eager", choices=["all", "select", "attend"], default=None,

@@ -34,6 +34,7 @@ EXPORTED = [
     "dsa_last_error", "dsa_version", "dsa_config_validate", "dsa_select_k", "dsa_out_width",
     "dsa_num_pools", "dsa_kpool_compress", "dsa_kpool_compress_fp8", "dsa_quantize_rows_fp8",
     "dsa_k_norm", "dsa_indexer_store", "dsa_write_geom", "dsa_pool_append",
+    "dsa_topk_to_mask", "dsa_mla_masked_attn",
     "dsa_compact_pools", "dsa_index_scores",
     "dsa_compact_index_scores",
     "dsa_topk_pools", "dsa_expand_selection", "dsa_topk_expand", "dsa_sparse_mla_decode_workspace",
@@ -87,6 +88,9 @@ def lib():
             "dsa_kpool_compress_fp8": ([_CFG, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P], _I),
             "dsa_quantize_rows_fp8": ([_I64, _I, _P, _I, _P, _P, _P], _I),
             "dsa_k_norm": ([_I64, _I, _P, _P, _P, _F, _P], _I),
+            "dsa_topk_to_mask": ([_I, _I, _I, _P, _P, _P], _I),
+            "dsa_mla_masked_attn": ([_CFG, _I, _I, _I, _F, _P, _P, _P, _P, _I, _P, _I64, _P, _I,
+                                     _I, _P, _P, _P], _I),
             "dsa_indexer_store": ([_I, _I, _I, _P, _P, _P, _P, _P, _P, _P], _I),
             "dsa_write_geom": ([_I, _P, _P, _P, _P], _I),
             "dsa_pool_append": ([_CFG, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
@@ -511,6 +515,49 @@ def sparse_mla_decode(cfg: Config, q_abs, token_ids, row_seq, kv, *, B: int, sm_
                                        _ptr(kv_scales) if code == DSA_FP8_E4M3 else None, rows,
                                        S, _ptr(block_table), max_blocks, block_size, _ptr(out),
                                        _ptr(lse), _ptr(ws), ws_bytes, _stream(q_abs)))
+    return out, lse
+
+
+def topk_to_mask(token_ids, S: int, mask=None):
+    """[Q, W] token ids -> [Q, S] u8 mask of the tokens present."""
+    _dev(token_ids, "token_ids", (torch.int32,))
+    Q, W = token_ids.shape
+    if mask is None:
+        mask = torch.empty((Q, S), dtype=torch.uint8, device=token_ids.device)
+    _dev(mask, "mask", (torch.uint8,), (Q, S))
+    _check(lib().dsa_topk_to_mask(Q, W, S, _ptr(token_ids), _ptr(mask), _stream(token_ids)))
+    return mask
+
+
+def mla_masked_attn(cfg: Config, q_abs, mask, row_seq, kv, *, B: int, sm_scale: float,
+                    kv_scales=None, block_table=None, block_size: int = 64, out=None, lse=None):
+    """Dense attention over every masked token (the cross-check of sparse_mla_decode): q_abs
+    [Q,H,512] bf16; mask [Q,S] u8; kv as sparse_mla_decode with S = mask width."""
+    _dev(q_abs, "q_abs", (torch.bfloat16,))
+    Q, H, C = q_abs.shape
+    if H != cfg.heads or C != 512:
+        raise ValueError("q_abs must be [Q, heads, 512]")
+    _dev(mask, "mask", (torch.uint8,))
+    S = mask.shape[1]
+    _dev(row_seq, "row_seq", (torch.int32,), (Q,))
+    _dev(kv, "kv", (torch.bfloat16,) + _FP8)
+    rows = kv.numel() // 512
+    code = _dtype_code(kv)
+    if code == DSA_FP8_E4M3:
+        _dev(kv_scales, "kv_scales", (torch.float32,))
+    max_blocks = 0
+    if block_table is not None:
+        _dev(block_table, "block_table", (torch.int32,))
+        max_blocks = block_table.shape[1]
+    if out is None:
+        out = torch.empty((Q, H, 512), dtype=torch.float32, device=q_abs.device)
+    if lse is None:
+        lse = torch.empty((Q, H), dtype=torch.float32, device=q_abs.device)
+    _check(lib().dsa_mla_masked_attn(ctypes.byref(cfg), Q, S, B, float(sm_scale), _ptr(q_abs),
+                                     _ptr(mask), _ptr(row_seq), _ptr(kv), code,
+                                     _ptr(kv_scales) if code == DSA_FP8_E4M3 else None, rows,
+                                     _ptr(block_table), max_blocks, block_size, _ptr(out),
+                                     _ptr(lse), _stream(q_abs)))
     return out, lse
 
 

@@ -173,6 +173,48 @@ int dsa_kpool_compress_fp8(const dsa_config *cfg, int B, int S, int first_key, c
                       "kpool_compress_fp8 launch");
 }
 
+int dsa_topk_to_mask(int Q, int W, int S, const int32_t *token_ids, uint8_t *mask,
+                     hipStream_t stream) {
+    clear_error();
+    if (Q < 0 || W < 0 || S < 0) return set_error(DSA_ERR_BAD_SIZE, "topk_to_mask: negative size");
+    if (Q == 0 || S == 0) return DSA_OK;
+    if (!mask || (W > 0 && !token_ids)) return set_error(DSA_ERR_NULL_ARG, "topk_to_mask: a buffer is NULL");
+    return hip_status(dsa::launch_topk_to_mask(Q, W, S, token_ids, mask, stream), "topk_to_mask launch");
+}
+
+int dsa_mla_masked_attn(const dsa_config *cfg, int Q, int S, int B, float sm_scale,
+                        const void *q_abs, const uint8_t *mask, const int32_t *row_seq,
+                        const void *kv, dsa_dtype kv_dtype, const float *kv_scales,
+                        int64_t kv_rows, const int32_t *block_table, int max_blocks,
+                        int block_size, float *out, float *lse, hipStream_t stream) {
+    clear_error();
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (Q < 0 || S < 0 || B < 0 || kv_rows < 0) return set_error(DSA_ERR_BAD_SIZE, "negative size");
+    if (S > DSA_MASKED_ATTN_MAX_KEYS)
+        return set_error(DSA_ERR_UNSUPPORTED, "mla_masked_attn: S = %d above the %d keys of the score row",
+                    S, DSA_MASKED_ATTN_MAX_KEYS);
+    if (kv_dtype != DSA_BF16 && kv_dtype != DSA_FP8_E4M3)
+        return set_error(DSA_ERR_BAD_DTYPE, "mla_masked_attn: latent must be bf16 or fp8 e4m3");
+    if (kv_rows > INT32_MAX) return set_error(DSA_ERR_UNSUPPORTED, "mla_masked_attn: kv_rows above 2^31 - 1");
+    if (Q == 0 || cfg->heads == 0) return DSA_OK;
+    const bool fp8 = kv_dtype == DSA_FP8_E4M3;
+    if (!q_abs || !row_seq || !out || (S > 0 && !mask))
+        return set_error(DSA_ERR_NULL_ARG, "mla_masked_attn: a buffer is NULL");
+    if (kv_rows > 0 && !kv) return set_error(DSA_ERR_NULL_ARG, "mla_masked_attn: kv is NULL");
+    if (fp8 && kv_rows > 0 && !kv_scales)
+        return set_error(DSA_ERR_NULL_ARG, "mla_masked_attn: fp8 latent needs kv_scales");
+    if (block_table && (block_size <= 0 || max_blocks < 0))
+        return set_error(DSA_ERR_BAD_SIZE, "mla_masked_attn: paged latent needs block_size > 0");
+    if (!aligned(q_abs, 16) || (kv && !aligned(kv, 16)) || !aligned(out, 8))
+        return set_error(DSA_ERR_BAD_SIZE, "mla_masked_attn: q_abs and kv need 16-byte alignment");
+    return hip_status(dsa::launch_masked_attn(Q, cfg->heads, S, B, sm_scale,
+                                              static_cast<const uint16_t *>(q_abs), mask, row_seq, kv,
+                                              fp8, kv_scales, kv_rows, block_table, max_blocks,
+                                              block_size, out, lse, stream),
+                      "mla_masked_attn launch");
+}
+
 int dsa_k_norm(int64_t rows, int D, void *x, const void *weight, const void *bias, float eps,
                hipStream_t stream) {
     clear_error();

@@ -31,6 +31,14 @@ hipError_t launch_indexer_store(int B, int S, int D, const int32_t *pos, const u
                                 uint8_t *valid, hipStream_t stream);
 hipError_t launch_write_geom(int B, const int32_t *seq_len, int32_t *row_seq, int32_t *row_pos,
                              hipStream_t stream);
+// The dense masked cross-check: token mask of a selection; attention over every masked token.
+hipError_t launch_topk_to_mask(int Q, int W, int S, const int32_t *token_ids, uint8_t *mask,
+                               hipStream_t stream);
+hipError_t launch_masked_attn(int Q, int H, int S, int B, float sm_scale, const uint16_t *q_abs,
+                              const uint8_t *mask, const int32_t *row_seq, const void *kv,
+                              bool kv_fp8, const float *kv_scales, int64_t kv_rows,
+                              const int32_t *block_table, int max_blocks, int block_size,
+                              float *out, float *lse, hipStream_t stream);
 // Rows of n values (bf16 or f32) -> e4m3 codes and per-row f32 scales.
 hipError_t launch_quantize_rows(long long rows, int n, const void *src, bool f32_src,
                                 uint8_t *codes, float *scales, hipStream_t stream);

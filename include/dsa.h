@@ -70,6 +70,10 @@ enum {
 /* Kernel limits of this library: indexer heads per call, index_head_dim values, and the
  * MLA heads handled per 32-head group (more heads run as several groups). */
 #define DSA_MAX_INDEX_HEADS 32
+/* Most keys dsa_mla_masked_attn takes: its [S] f32 score row sits in 128 KiB of LDS
+ * (the pages' kernel: 12,288 in 48 KB, mod.rs MASKED_ATTN_MAX_KEYS). */
+#define DSA_MASKED_ATTN_MAX_KEYS 32768
+
 /* Widest token selection (W, token slots per row) dsa_sparse_mla_decode accepts. */
 #define DSA_MAX_MLA_WIDTH 32768
 
@@ -284,6 +288,29 @@ int dsa_sparse_mla_decode(const dsa_config *cfg, int Q, int W, int B, float sm_s
                           int64_t kv_rows, int S, const int32_t *block_table, int max_blocks,
                           int block_size, float *out, float *lse, void *ws, size_t ws_bytes,
                           hipStream_t stream);
+
+/* ------------------------------------------------------------------ dense masked cross-check */
+/* mod.rs, Glm5NextDsaKernels::{topk_to_mask, mla_masked_attn} and MASKED_ATTN_MAX_KEYS: the
+ * selection as a token mask, and a dense attention over every masked token that stages the
+ * whole [S] score row; a second route to dsa_sparse_mla_decode's result, used to check it.
+ *
+ * topk_to_mask: mask[r, t] = 1 when some slot of token_ids[r] holds t (0 <= t < S), else 0;
+ * every element written. token_ids: [Q, W] i32; mask: [Q, S] u8. */
+int dsa_topk_to_mask(int Q, int W, int S, const int32_t *token_ids, uint8_t *mask,
+                     hipStream_t stream);
+
+/* mla_masked_attn: for row r and head h, over every t < S with mask[r, t] = 1 (ascending),
+ * logit_t = sm_scale * q_abs[r,h,:] . v_t and out[r,h,:] = sum_t softmax_t v_t,
+ * lse[r,h] = log sum exp(logit); latent rows, dtypes, paging and skipped rows exactly as
+ * dsa_sparse_mla_decode (S is also the contiguous stride). A row without a token gives
+ * out = 0, lse = -inf. S above DSA_MASKED_ATTN_MAX_KEYS is refused (DSA_ERR_UNSUPPORTED).
+ * q_abs: [Q, heads, 512] bf16; mask: [Q, S] u8; out: [Q, heads, 512] f32; lse: [Q, heads]
+ * f32 or NULL. One block per (row, head), f32 arithmetic: a check, not the decode path. */
+int dsa_mla_masked_attn(const dsa_config *cfg, int Q, int S, int B, float sm_scale,
+                        const void *q_abs, const uint8_t *mask, const int32_t *row_seq,
+                        const void *kv, dsa_dtype kv_dtype, const float *kv_scales,
+                        int64_t kv_rows, const int32_t *block_table, int max_blocks,
+                        int block_size, float *out, float *lse, hipStream_t stream);
 
 /* ------------------------------------------------------------------ host weight prep */
 /* build.rs, absorb_q / absorb_q_rows (host memory, f32): q_absorb[h*kvl + c][k] =

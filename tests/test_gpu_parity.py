@@ -527,6 +527,58 @@ def test_quantize_rows_fp8_bit_exact(n):
                                    src[tuple(bad[0])] / rs[bad[0][0]])
 
 
+# ------------------------------------------------------------------ dense masked cross-check
+
+@pytest.mark.parametrize("name", ALL)
+def test_topk_to_mask_bit_exact(name):
+    di, x, _, _ = case(name)
+    wl = di.wl
+    tok = synth.draw_token_ids(di)
+    rows = _rows(di, 30)
+    tok = np.ascontiguousarray(tok[rows])
+    tok[0, :5] = [wl.S, wl.S + 7, -3, tok[0, 5], tok[0, 5]]   # out of range and duplicates
+    m = dsa.topk_to_mask(_dev(tok), wl.S)
+    assert np.array_equal(m.cpu().numpy(), oracle.topk_to_mask(tok, wl.S))
+
+
+MASKED = ["tiny", "ragged_bf16", "ragged_fp8", "ragged_prefill", "decode_b8_32k"]
+
+
+@pytest.mark.parametrize("name", MASKED)
+def test_masked_attn_against_oracle_and_sparse_decode(name):
+    """The dense masked attention against the oracle's (sampled rows), and the cross-check
+    itself: sparse decode over token ids and dense attention over their mask agree within the
+    decode tolerance on every row."""
+    di, x, _, _ = case(name)
+    wl = di.wl
+    cfg = config_for(wl)
+    tok = synth.draw_token_ids(di)
+    mask = dsa.topk_to_mask(_dev(tok), wl.S)
+    kw = dict(sm_scale=di.sm_scale, kv_scales=x.kv_scales, block_table=x.block_table)
+    mo, ml = dsa.mla_masked_attn(cfg, x.q_abs, mask, x.row_seq, x.kv, B=wl.B, **kw)
+    rows = _rows(di, 6)
+    ro, rl = oracle.masked_attn(di.q_abs[rows], oracle.topk_to_mask(tok[rows], wl.S),
+                                di.row_seq[rows], di.kv, sm_scale=di.sm_scale,
+                                kv_scales=di.kv_scales, block_table=di.block_table)
+    _check_mla(mo.cpu().numpy()[rows], ml.cpu().numpy()[rows], ro, rl, wl.kv_fp8)
+    so, sl = dsa.sparse_mla_decode(cfg, x.q_abs, _dev(tok), x.row_seq, x.kv, B=wl.B, S=wl.S, **kw)
+    _check_mla(so.cpu().numpy(), sl.cpu().numpy(), mo.cpu().numpy().astype(np.float64),
+               ml.cpu().numpy().astype(np.float64), wl.kv_fp8)
+
+
+def test_masked_attn_empty_rows_and_the_key_limit():
+    di, x, _, _ = case("ragged_bf16")
+    wl = di.wl
+    cfg = config_for(wl)
+    mask = torch.zeros((wl.Q, wl.S), dtype=torch.uint8, device="cuda")
+    o, l = dsa.mla_masked_attn(cfg, x.q_abs, mask, x.row_seq, x.kv, B=wl.B, sm_scale=di.sm_scale)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(l))
+    big = torch.zeros((1, 32769), dtype=torch.uint8, device="cuda")
+    with pytest.raises(dsa.DsaError):
+        dsa.mla_masked_attn(cfg, x.q_abs[:1].contiguous(), big, x.row_seq[:1].contiguous(), x.kv,
+                            B=wl.B, sm_scale=di.sm_scale)
+
+
 # ------------------------------------------------------------------ decode-time upkeep
 
 def _bf(a):

@@ -190,3 +190,37 @@ def test_refusals_return_codes_without_launching():
     assert L.dsa_index_scores(c, 0, 1, 8, 0, 1.0, _NULL, _NULL, _NULL, _NULL, _NULL, 0, _NULL,
                               _NULL, _NULL, _NULL, _NULL, _NULL) == 0
     assert L.dsa_compact_pools(0, 8, _NULL, _NULL, _NULL, _NULL) == 0
+
+
+def test_refusals_of_the_fp8_writers_upkeep_and_masked_check():
+    """Refused before any launch (no GPU needed): shapes the kernels are not built for, null
+    buffers, bad dtypes, negative sizes."""
+    L = dsa.lib()
+    cfg = _cfg()
+    c = ctypes.byref(cfg)
+    # fp8 pooling: D not a power of two; null scales
+    assert L.dsa_kpool_compress_fp8(ctypes.byref(_cfg(index_head_dim=48)), 1, 64, 0, _FAKE, _FAKE,
+                                    _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _NULL) == -14
+    assert L.dsa_kpool_compress_fp8(c, 1, 64, 0, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _NULL, _FAKE,
+                                    _NULL) == -1
+    # quantizer: n not a multiple of 8, too wide, bad dtype, negative rows
+    assert L.dsa_quantize_rows_fp8(4, 12, _FAKE, 0, _FAKE, _FAKE, _NULL) == -14
+    assert L.dsa_quantize_rows_fp8(4, 4104, _FAKE, 0, _FAKE, _FAKE, _NULL) == -14
+    assert L.dsa_quantize_rows_fp8(4, 512, _FAKE, 2, _FAKE, _FAKE, _NULL) == -3
+    assert L.dsa_quantize_rows_fp8(-1, 512, _FAKE, 0, _FAKE, _FAKE, _NULL) == -2
+    assert L.dsa_quantize_rows_fp8(0, 512, _NULL, 0, _NULL, _NULL, _NULL) == 0
+    # k_norm: D not 8 times a power of two; negative eps
+    assert L.dsa_k_norm(4, 96, _FAKE, _FAKE, _FAKE, ctypes.c_float(1e-5), _NULL) == -14
+    assert L.dsa_k_norm(4, 128, _FAKE, _FAKE, _FAKE, ctypes.c_float(-1.0), _NULL) == -2
+    # indexer_store / write_geom / pool_append nulls
+    assert L.dsa_indexer_store(2, 8, 128, _NULL, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _NULL) == -1
+    assert L.dsa_write_geom(2, _FAKE, _NULL, _FAKE, _NULL) == -1
+    assert L.dsa_pool_append(c, 2, 64, 0, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE, _NULL, _FAKE,
+                             _NULL, _FAKE, _NULL) == -1
+    # masked attention: more keys than the score row holds; fp8 without scales
+    assert L.dsa_mla_masked_attn(c, 1, 32769, 1, ctypes.c_float(0.0625), _FAKE, _FAKE, _FAKE,
+                                 _FAKE, 0, _NULL, 1 << 20, _NULL, 0, 64, _FAKE, _NULL,
+                                 _NULL) == -14
+    assert L.dsa_mla_masked_attn(c, 1, 64, 1, ctypes.c_float(0.0625), _FAKE, _FAKE, _FAKE, _FAKE,
+                                 2, _NULL, 64, _NULL, 0, 64, _FAKE, _NULL, _NULL) == -1
+    assert L.dsa_topk_to_mask(1, 4, 64, _FAKE, _NULL, _NULL) == -1
