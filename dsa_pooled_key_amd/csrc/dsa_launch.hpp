@@ -76,7 +76,7 @@ hipError_t launch_expand_selection(int Q, int Kw, int KP, int topk, int W, bool 
                                    const uint8_t *valid, int32_t *token_ids, hipStream_t stream);
 
 // Sparse MLA split limits: token slots one block resolves up front, splits per row.
-constexpr int kMlaMaxSplit = 512;
+constexpr int kMlaMaxSplit = 2048;
 constexpr int kMlaMaxSplits = 64;
 static_assert(kMlaMaxSplit * kMlaMaxSplits >= DSA_MAX_MLA_WIDTH, "widest selection must fit");
 
