@@ -37,7 +37,8 @@ EXPORTED = [
     "dsa_topk_to_mask", "dsa_mla_masked_attn",
     "dsa_compact_pools", "dsa_index_scores",
     "dsa_compact_index_scores",
-    "dsa_topk_pools", "dsa_expand_selection", "dsa_topk_expand", "dsa_sparse_mla_decode_workspace",
+    "dsa_topk_workspace", "dsa_topk_pools", "dsa_expand_selection", "dsa_topk_expand",
+    "dsa_sparse_mla_decode_workspace",
     "dsa_sparse_mla_decode", "dsa_absorb_q", "dsa_absorb_o", "dsa_f32_to_bf16_rne",
 ]
 
@@ -99,9 +100,11 @@ def lib():
                                   _P, _P, _P], _I),
             "dsa_compact_index_scores": ([_CFG, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P,
                                           _P, _P, _P, _P], _I),
-            "dsa_topk_pools": ([_CFG, _I, _I, _P, _P, _P, _P], _I),
+            "dsa_topk_workspace": ([_CFG, _I, _I], _SZ),
+            "dsa_topk_pools": ([_CFG, _I, _I, _P, _P, _P, _P, _SZ, _P], _I),
             "dsa_expand_selection": ([_CFG, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P], _I),
-            "dsa_topk_expand": ([_CFG, _I, _I, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P], _I),
+            "dsa_topk_expand": ([_CFG, _I, _I, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ,
+                                 _P], _I),
             "dsa_sparse_mla_decode_workspace": ([_CFG, _I, _I], _SZ),
             "dsa_sparse_mla_decode": ([_CFG, _I, _I, _I, _F, _P, _P, _P, _P, _I, _P, _I64, _I,
                                        _P, _I, _I, _P, _P, _P, _SZ, _P], _I),
@@ -404,7 +407,23 @@ def compact_index_scores(cfg: Config, q, w, row_seq, row_pos, keys, pool_valid, 
     return scores, cand
 
 
-def topk_pools(cfg: Config, scores, cand, sel=None):
+def topk_workspace(cfg: Config, Q: int, P: int) -> int:
+    """Bytes of the top-k workspace (0: one block a row, no workspace used)."""
+    return int(lib().dsa_topk_workspace(ctypes.byref(cfg), Q, P))
+
+
+def _topk_ws(cfg, Q, P, ws, device):
+    """The caller's workspace, or a fresh one of the size the call can use (None if 0);
+    ws=False asks for the one-block-a-row selection."""
+    if ws is False:
+        return None, 0
+    if ws is None:
+        need = topk_workspace(cfg, Q, P)
+        ws = torch.empty((need,), dtype=torch.uint8, device=device) if need else None
+    return ws, (0 if ws is None else ws.numel() * ws.element_size())
+
+
+def topk_pools(cfg: Config, scores, cand, sel=None, ws=None):
     """scores [Q,P] f32, cand [Q,P] u8 -> sel [Q, select_k(P)] i32 (ascending, -1 padded)."""
     _dev(scores, "scores", (torch.float32,))
     Q, P = scores.shape
@@ -413,8 +432,9 @@ def topk_pools(cfg: Config, scores, cand, sel=None):
     if sel is None:
         sel = torch.empty((Q, kw), dtype=torch.int32, device=scores.device)
     _dev(sel, "sel", (torch.int32,), (Q, kw))
+    ws, ws_bytes = _topk_ws(cfg, Q, P, ws, scores.device)
     _check(lib().dsa_topk_pools(ctypes.byref(cfg), Q, P, _ptr(scores), _ptr(cand), _ptr(sel),
-                                _stream(scores)))
+                                _ptr(ws), ws_bytes, _stream(scores)))
     return sel
 
 
@@ -440,7 +460,7 @@ def expand_selection(cfg: Config, sel, row_seq, row_pos, valid, *, S: int, first
 
 
 def topk_expand(cfg: Config, scores, cand, row_seq, row_pos, valid, *, S: int, first_key: int,
-                sel=None, token_ids=None):
+                sel=None, token_ids=None, ws=None):
     """Fused top-k and expansion: the same (sel, token_ids) as topk_pools then
     expand_selection. scores/cand [Q,P]; valid [B,S] u8 (read for the tail)."""
     _dev(scores, "scores", (torch.float32,))
@@ -460,9 +480,10 @@ def topk_expand(cfg: Config, scores, cand, row_seq, row_pos, valid, *, S: int, f
         token_ids = torch.empty((Q, W), dtype=torch.int32, device=scores.device)
     _dev(sel, "sel", (torch.int32,), (Q, kw))
     _dev(token_ids, "token_ids", (torch.int32,), (Q, W))
+    ws, ws_bytes = _topk_ws(cfg, Q, P, ws, scores.device)
     _check(lib().dsa_topk_expand(ctypes.byref(cfg), Q, P, _ptr(scores), _ptr(cand), B, S,
                                  first_key, _ptr(row_seq), _ptr(row_pos), _ptr(valid), _ptr(sel),
-                                 _ptr(token_ids), _stream(scores)))
+                                 _ptr(token_ids), _ptr(ws), ws_bytes, _stream(scores)))
     return sel, token_ids
 
 

@@ -373,8 +373,14 @@ int dsa_compact_index_scores(const dsa_config *cfg, int Q, int B, int P, int fir
                       "compact_index_scores launch");
 }
 
+size_t dsa_topk_workspace(const dsa_config *cfg, int Q, int P) {
+    clear_error();
+    if (check_config(cfg) || Q < 0 || P < 0 || P > dsa::kTopkMaxPools) return 0;
+    return dsa::topk_workspace_bytes(Q, P, (int)select_k(cfg, P));
+}
+
 int dsa_topk_pools(const dsa_config *cfg, int Q, int P, const float *scores, const uint8_t *cand,
-                   int32_t *sel, hipStream_t stream) {
+                   int32_t *sel, void *ws, size_t ws_bytes, hipStream_t stream) {
     clear_error();
     int rc = check_config(cfg);
     if (rc) return rc;
@@ -385,7 +391,9 @@ int dsa_topk_pools(const dsa_config *cfg, int Q, int P, const float *scores, con
     const int Kw = (int)select_k(cfg, P);
     if (Q == 0 || Kw == 0) return DSA_OK;
     if (!scores || !cand || !sel) return set_error(DSA_ERR_NULL_ARG, "topk_pools: a buffer is NULL");
-    return hip_status(dsa::launch_topk_pools(Q, P, Kw, scores, cand, sel, stream),
+    if (ws_bytes > 0 && (!ws || !aligned(ws, 16)))
+        return set_error(DSA_ERR_WORKSPACE, "topk_pools: a workspace needs a 16-byte aligned pointer");
+    return hip_status(dsa::launch_topk_pools(Q, P, Kw, scores, cand, sel, ws, ws_bytes, stream),
                       "topk_pools launch");
 }
 
@@ -413,7 +421,8 @@ int dsa_expand_selection(const dsa_config *cfg, int Q, int Kw, int B, int S, int
 
 int dsa_topk_expand(const dsa_config *cfg, int Q, int P, const float *scores, const uint8_t *cand,
                     int B, int S, int first_key, const int32_t *row_seq, const int32_t *row_pos,
-                    const uint8_t *valid, int32_t *sel, int32_t *token_ids, hipStream_t stream) {
+                    const uint8_t *valid, int32_t *sel, int32_t *token_ids, void *ws,
+                    size_t ws_bytes, hipStream_t stream) {
     clear_error();
     int rc = check_config(cfg);
     if (rc) return rc;
@@ -430,9 +439,11 @@ int dsa_topk_expand(const dsa_config *cfg, int Q, int P, const float *scores, co
     const bool tail = cfg->always_select_tail != 0;
     if (!token_ids || (Kw > 0 && (!scores || !cand || !sel)) || (tail && (!row_seq || !row_pos || !valid)))
         return set_error(DSA_ERR_NULL_ARG, "topk_expand: a buffer is NULL");
+    if (ws_bytes > 0 && (!ws || !aligned(ws, 16)))
+        return set_error(DSA_ERR_WORKSPACE, "topk_expand: a workspace needs a 16-byte aligned pointer");
     return hip_status(dsa::launch_topk_expand(Q, P, Kw, scores, cand, sel, cfg->index_kpool,
                                               cfg->index_topk, (int)W, tail, B, S, first_key, row_seq,
-                                              row_pos, valid, token_ids, stream),
+                                              row_pos, valid, token_ids, ws, ws_bytes, stream),
                       "topk_expand launch");
 }
 

@@ -61,14 +61,17 @@ hipError_t launch_index_scores_valid(int Q, int B, int P, int Hi, int D, int KP,
 
 // Largest row length the top-k kernel keeps in registers.
 constexpr int kTopkMaxPools = 65536;
+// Workspace of the two-stage selection for few long rows (0 when one block a row runs).
+size_t topk_workspace_bytes(int Q, int P, int Kw);
 hipError_t launch_topk_pools(int Q, int P, int Kw, const float *scores, const uint8_t *cand,
-                             int32_t *sel, hipStream_t stream);
+                             int32_t *sel, void *ws, size_t ws_bytes, hipStream_t stream);
 
 // Top-k and token-id expansion in one kernel (same results as the two calls in sequence).
 hipError_t launch_topk_expand(int Q, int P, int Kw, const float *scores, const uint8_t *cand,
                               int32_t *sel, int KP, int topk, int W, bool tail, int B, int S,
                               int first_key, const int32_t *row_seq, const int32_t *row_pos,
-                              const uint8_t *valid, int32_t *token_ids, hipStream_t stream);
+                              const uint8_t *valid, int32_t *token_ids, void *ws,
+                              size_t ws_bytes, hipStream_t stream);
 
 hipError_t launch_expand_selection(int Q, int Kw, int KP, int topk, int W, bool tail, int B,
                                    int S, int first_key, int P, const int32_t *sel,

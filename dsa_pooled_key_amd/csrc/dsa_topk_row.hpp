@@ -90,12 +90,15 @@ __device__ __forceinline__ void load_keys(int P, int vec, const float *__restric
     }
 }
 
-// Row r's selection from its keys (thread t: pools t*KPT ..). Writes sel[r, 0..Kw) and, with
-// EXPAND, token_ids[r, 0..W). Called by all kThreads threads of the block.
+// Row r's selection from its keys (thread t: key slots t*KPT ..). Writes sel[r, 0..Kw) and,
+// with EXPAND, token_ids[r, 0..W). Key slot i stands for pool pool0 + i, or for pool ids[i]
+// when an id table (LDS, ascending over the slots that hold candidates) is given; ties go to
+// the lower slot either way. Called by all kThreads threads of the block.
 template <int KPT, bool EXPAND>
 __device__ __forceinline__ void select_row(int r, int P, int Kw, uint32_t (&key)[KPT],
                                            int32_t *__restrict__ sel, const ExpandArgs &ex,
-                                           Smem &sm) {
+                                           Smem &sm, int pool0 = 0,
+                                           const int *ids = nullptr) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
@@ -325,12 +328,13 @@ __device__ __forceinline__ void select_row(int r, int P, int Kw, uint32_t (&key)
             }
         }
     };
+    auto pool_of = [&](int i) { return ids != nullptr ? ids[base + i] : pool0 + base + i; };
     if (Kw <= kStageSel) {
         // The ids go to LDS at their positions; after one barrier thread j writes position j,
         // so a row whose selection sits in few threads (a context of few pools) still spreads
         // its stores over the block, and ids and token ids go out in coalesced runs.
         while (smask != 0u && o < Kw) {
-            sm.sel_s[o++] = base + __builtin_ctzll(smask);
+            sm.sel_s[o++] = pool_of(__builtin_ctzll(smask));
             smask &= smask - 1ull;
         }
         __syncthreads();
@@ -340,7 +344,7 @@ __device__ __forceinline__ void select_row(int r, int P, int Kw, uint32_t (&key)
         }
     } else {
         while (smask != 0u && o < Kw) {
-            write_pool(o, base + __builtin_ctzll(smask));
+            write_pool(o, pool_of(__builtin_ctzll(smask)));
             smask &= smask - 1ull;
             ++o;
         }

@@ -31,6 +31,64 @@ __global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int
     select_row<KPT, EXPAND>(r, P, Kw, key, sel, ex, sm);
 }
 
+// Two stages for rows that are few and long, which a block each would leave most of the chip
+// idle for: stage 1 splits every row into segments of kSegPools pools and selects each
+// segment's best Kw exactly (block (r, s), the same selection); every pool of the row's best Kw
+// is among its segment's best Kw. Stage 2 selects the row's best Kw from the segments' picks
+// (their scores gathered again by id) and expands them. Segments are in pool order and each
+// lists its picks ascending, so the slot order of stage 2 is pool order and ties keep
+// going to the lower pool.
+constexpr int kSegKpt = 8;
+constexpr int kSegPools = kThreads * kSegKpt;
+
+__global__ __launch_bounds__(kThreads) void topk_segment_kernel(int P, int Kw, int nseg, int vec,
+                                                                const float *__restrict__ scores,
+                                                                const uint8_t *__restrict__ cand,
+                                                                int32_t *__restrict__ picks) {
+    __shared__ Smem sm;
+    const int r = blockIdx.x, sg = blockIdx.y;
+    const int p0 = sg * kSegPools;
+    const int n = min(kSegPools, P - p0);
+    uint32_t key[kSegKpt];
+    load_keys<kSegKpt>(n, vec, scores + (size_t)r * P + p0, cand + (size_t)r * P + p0, key);
+    select_row<kSegKpt, false>(r * nseg + sg, n, Kw, key, picks, ExpandArgs{}, sm, p0);
+}
+
+template <int KPT, bool EXPAND>
+__global__ __launch_bounds__(kThreads) void topk_merge_kernel(int P, int Kw, int n,
+                                                              const float *__restrict__ scores,
+                                                              const int32_t *__restrict__ picks,
+                                                              int32_t *__restrict__ sel,
+                                                              ExpandArgs ex) {
+    __shared__ Smem sm;
+    __shared__ int ids_s[kThreads * KPT];
+    const int r = blockIdx.x;
+    const int base = threadIdx.x * KPT;
+    int id[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int e = base + i;
+        const int v = e < n ? picks[(size_t)r * n + e] : -1;
+        id[i] = v >= 0 && v < P ? v : -1;
+        ids_s[e] = id[i];
+    }
+    uint32_t key[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) key[i] = id[i] >= 0 ? ordered_key(scores[(size_t)r * P + id[i]]) : 0u;
+    select_row<KPT, EXPAND>(r, n, Kw, key, sel, ex, sm, 0, ids_s);
+}
+
+// Segments a row for the two-stage selection, or 0 for one block a row. Two stages pay for
+// few rows of more than 16,384 pools (one block holds 32 or 64 keys a thread there);
+// measured on 32 rows of 16,384 pools one block a row is faster (10.2 against 13.6 us).
+int topk_segments(int Q, int P, int Kw) {
+    const int nseg = (P + kSegPools - 1) / kSegPools;
+    if (Q > 64 || P <= 16384 || nseg < 2 || 4 * Kw > kSegPools ||
+        (long long)nseg * Kw > 8 * kThreads)
+        return 0;
+    return nseg;
+}
+
 template <int KPT>
 hipError_t launch_kpt(int Q, int P, int Kw, const float *scores, const uint8_t *cand,
                       int32_t *sel, const ExpandArgs *ex, hipStream_t stream) {
@@ -48,9 +106,41 @@ hipError_t launch_kpt(int Q, int P, int Kw, const float *scores, const uint8_t *
     return hipGetLastError();
 }
 
+template <int KPT>
+hipError_t launch_merge(int Q, int P, int Kw, int n, const float *scores, const int32_t *picks,
+                        int32_t *sel, const ExpandArgs *ex, hipStream_t stream) {
+    if (ex)
+        hipLaunchKernelGGL((topk_merge_kernel<KPT, true>), dim3(Q), dim3(kThreads), 0, stream, P, Kw,
+                           n, scores, picks, sel, *ex);
+    else
+        hipLaunchKernelGGL((topk_merge_kernel<KPT, false>), dim3(Q), dim3(kThreads), 0, stream, P, Kw,
+                           n, scores, picks, sel, ExpandArgs{});
+    return hipGetLastError();
+}
+
+hipError_t launch_two_stage(int Q, int P, int Kw, int nseg, const float *scores,
+                            const uint8_t *cand, int32_t *sel, const ExpandArgs *ex, void *ws,
+                            hipStream_t stream) {
+    int32_t *picks = static_cast<int32_t *>(ws);
+    const int vec = (kSegPools & 15) == 0 && (P & 15) == 0 && (reinterpret_cast<uintptr_t>(cand) & 15) == 0 &&
+                    (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+    hipLaunchKernelGGL(topk_segment_kernel, dim3(Q, nseg), dim3(kThreads), 0, stream, P, Kw, nseg, vec,
+                       scores, cand, picks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n = nseg * Kw;
+    if (n <= kThreads * 2) return launch_merge<2>(Q, P, Kw, n, scores, picks, sel, ex, stream);
+    if (n <= kThreads * 4) return launch_merge<4>(Q, P, Kw, n, scores, picks, sel, ex, stream);
+    return launch_merge<8>(Q, P, Kw, n, scores, picks, sel, ex, stream);
+}
+
 hipError_t launch_any(int Q, int P, int Kw, const float *scores, const uint8_t *cand,
-                      int32_t *sel, const ExpandArgs *ex, hipStream_t stream) {
+                      int32_t *sel, const ExpandArgs *ex, void *ws, size_t ws_bytes,
+                      hipStream_t stream) {
     if (Q == 0 || Kw == 0) return hipSuccess;
+    const int nseg = topk_segments(Q, P, Kw);
+    if (nseg > 0 && ws != nullptr && ws_bytes >= topk_workspace_bytes(Q, P, Kw))
+        return launch_two_stage(Q, P, Kw, nseg, scores, cand, sel, ex, ws, stream);
     if (P <= kThreads * 1) return launch_kpt<1>(Q, P, Kw, scores, cand, sel, ex, stream);
     if (P <= kThreads * 2) return launch_kpt<2>(Q, P, Kw, scores, cand, sel, ex, stream);
     if (P <= kThreads * 4) return launch_kpt<4>(Q, P, Kw, scores, cand, sel, ex, stream);
@@ -63,15 +153,21 @@ hipError_t launch_any(int Q, int P, int Kw, const float *scores, const uint8_t *
 
 }  // namespace
 
+size_t topk_workspace_bytes(int Q, int P, int Kw) {
+    const int nseg = topk_segments(Q, P, Kw);
+    return nseg > 0 ? (size_t)Q * nseg * Kw * sizeof(int32_t) : 0;
+}
+
 hipError_t launch_topk_pools(int Q, int P, int Kw, const float *scores, const uint8_t *cand,
-                             int32_t *sel, hipStream_t stream) {
-    return launch_any(Q, P, Kw, scores, cand, sel, nullptr, stream);
+                             int32_t *sel, void *ws, size_t ws_bytes, hipStream_t stream) {
+    return launch_any(Q, P, Kw, scores, cand, sel, nullptr, ws, ws_bytes, stream);
 }
 
 hipError_t launch_topk_expand(int Q, int P, int Kw, const float *scores, const uint8_t *cand,
                               int32_t *sel, int KP, int topk, int W, bool tail, int B, int S,
                               int first_key, const int32_t *row_seq, const int32_t *row_pos,
-                              const uint8_t *valid, int32_t *token_ids, hipStream_t stream) {
+                              const uint8_t *valid, int32_t *token_ids, void *ws,
+                              size_t ws_bytes, hipStream_t stream) {
     if (Q == 0 || W == 0) return hipSuccess;
     if (Kw == 0)  // nothing to select: the plain expansion writes the -1 row and the tail
         return launch_expand_selection(Q, 0, KP, topk, W, tail, B, S, first_key, P, sel, row_seq,
@@ -79,7 +175,7 @@ hipError_t launch_topk_expand(int Q, int P, int Kw, const float *scores, const u
     const int vec8 = KP == 8 && (W & 3) == 0 && (reinterpret_cast<uintptr_t>(token_ids) & 15) == 0;
     const ExpandArgs ex{KP, topk, W, tail ? 1 : 0, B, S, first_key, vec8, row_seq, row_pos, valid,
                         token_ids};
-    return launch_any(Q, P, Kw, scores, cand, sel, &ex, stream);
+    return launch_any(Q, P, Kw, scores, cand, sel, &ex, ws, ws_bytes, stream);
 }
 
 }  // namespace dsa

@@ -81,6 +81,8 @@ class DecodeStep:
         self.token_ids = torch.empty((Q, self.width), dtype=torch.int32, device=dev)
         self.out = torch.empty((Q, wl.heads, 512), dtype=torch.float32, device=dev)
         self.lse = torch.empty((Q, wl.heads), dtype=torch.float32, device=dev)
+        tk = dsa.topk_workspace(self.cfg, Q, P)
+        self.topk_ws = torch.empty((tk,), dtype=torch.uint8, device=dev) if tk else None
         need = dsa.sparse_mla_workspace(self.cfg, Q, self.width)
         self.ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
 
@@ -104,9 +106,11 @@ class DecodeStep:
         x, wl = self.x, self.wl
         if self.fused:
             dsa.topk_expand(self.cfg, self.scores, self.cand, x.row_seq, x.row_pos, x.valid,
-                            S=wl.S, first_key=wl.first_key, sel=self.sel, token_ids=self.token_ids)
+                            S=wl.S, first_key=wl.first_key, sel=self.sel, token_ids=self.token_ids,
+                            ws=self.topk_ws if self.topk_ws is not None else False)
         else:
-            dsa.topk_pools(self.cfg, self.scores, self.cand, self.sel)
+            dsa.topk_pools(self.cfg, self.scores, self.cand, self.sel,
+                           ws=self.topk_ws if self.topk_ws is not None else False)
             dsa.expand_selection(self.cfg, self.sel, x.row_seq, x.row_pos, x.valid, S=wl.S,
                                  first_key=wl.first_key, token_ids=self.token_ids)
 

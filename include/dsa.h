@@ -239,9 +239,15 @@ int dsa_compact_index_scores(const dsa_config *cfg, int Q, int B, int P, int fir
  * rank first by (score descending, pool index ascending) are written in ascending pool order,
  * then -1 up to Kw. Equal scores (-0 == +0) go to the lower pool index, the tie rule tp.rs
  * shows is needed for a stable selection. Kw = dsa_select_k(cfg, P).
- * scores: [Q, P] f32; cand: [Q, P] u8; sel: [Q, Kw] i32. Scores must not be NaN. */
+ * scores: [Q, P] f32; cand: [Q, P] u8; sel: [Q, Kw] i32. Scores must not be NaN.
+ * ws: device workspace of dsa_topk_workspace(cfg, Q, P) bytes (16-byte aligned), or NULL with
+ * ws_bytes 0. Given it, few long rows (at most 64 rows of several 4,096-pool segments) are
+ * selected in two launches: each segment's best Kw first (one block per row and segment),
+ * then the row's best Kw among those; without it, or when too small, one block per row selects
+ * from the whole row. Both give the same sel. */
+size_t dsa_topk_workspace(const dsa_config *cfg, int Q, int P);
 int dsa_topk_pools(const dsa_config *cfg, int Q, int P, const float *scores, const uint8_t *cand,
-                   int32_t *sel, hipStream_t stream);
+                   int32_t *sel, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------ step 5 */
 /* mod.rs, "Shape of the pipeline" and "Checkpoint and kernel facts": token ids of the selected
@@ -259,10 +265,12 @@ int dsa_expand_selection(const dsa_config *cfg, int Q, int Kw, int B, int S, int
  * same sel [Q, Kw] (Kw = dsa_select_k(cfg, P)) as dsa_topk_pools and the same token_ids
  * [Q, dsa_out_width(cfg)] as dsa_expand_selection given that sel; the selection is not read
  * back from memory. P must not exceed dsa_num_pools(S, first_key, kpool) (DSA_ERR_BAD_SIZE).
- * Arguments as in the two calls; scores, cand and sel may be NULL only when Kw = 0. */
+ * Arguments as in the two calls; scores, cand and sel may be NULL only when Kw = 0. The
+ * workspace as dsa_topk_pools's (dsa_topk_workspace), or NULL. */
 int dsa_topk_expand(const dsa_config *cfg, int Q, int P, const float *scores, const uint8_t *cand,
                     int B, int S, int first_key, const int32_t *row_seq, const int32_t *row_pos,
-                    const uint8_t *valid, int32_t *sel, int32_t *token_ids, hipStream_t stream);
+                    const uint8_t *valid, int32_t *sel, int32_t *token_ids, void *ws,
+                    size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------ step 6 */
 /* build.rs, "The transforms" 1 and 3, and mod.rs (NoPE, 512-wide latent, attention restricted

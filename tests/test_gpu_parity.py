@@ -310,6 +310,35 @@ def test_topk_ties_signs_and_row_lengths(P, kw, seed):
     assert np.array_equal(ftok.cpu().numpy(), tok_ref)
 
 
+@pytest.mark.parametrize("P,kw,seed", [(16385, 512, 20), (24577, 512, 21), (32768, 512, 22),
+                                       (65536, 512, 23), (40000, 100, 24), (32768, 2048, 25)])
+def test_topk_two_stage_equals_one_block(P, kw, seed):
+    """The two-launch selection (segments' best, then the row's best among them) against the
+    one-block selection and the oracle, on rows with heavy ties across segment boundaries,
+    equal scores only in some segments, and rows with fewer candidates than kw."""
+    rng = np.random.default_rng(seed)
+    Q = 5
+    scores = (rng.integers(-6, 7, (Q, P)) / 4.0).astype(np.float32)
+    scores[1] = rng.standard_normal(P).astype(np.float32)
+    scores[2, : P // 2] = 1.0                                  # one value over several segments
+    cand = (rng.random((Q, P)) < 0.8).astype(np.uint8)
+    cand[3] = 0
+    cand[3, rng.choice(P, kw // 2, replace=False)] = 1         # fewer than kw
+    cand[4] = 0
+    scores[cand == 0] = -np.inf
+    cfg = dsa.Config.make(index_heads=32, index_head_dim=128, index_kpool=1, index_topk=kw,
+                          heads=32)
+    assert dsa.topk_workspace(cfg, Q, P) > 0
+    two = dsa.topk_pools(cfg, _dev(scores), _dev(cand)).cpu().numpy()
+    one = dsa.topk_pools(cfg, _dev(scores), _dev(cand), ws=False).cpu().numpy()
+    ref = oracle.topk_pools(scores, cand, min(kw, P))
+    assert np.array_equal(two, ref) and np.array_equal(one, ref)
+    zeros = _dev(np.zeros(Q, np.int32))
+    fsel, ftok = dsa.topk_expand(cfg, _dev(scores), _dev(cand), zeros, zeros,
+                                 _dev(np.ones((1, P), np.uint8)), S=P, first_key=0)
+    assert np.array_equal(fsel.cpu().numpy(), ref)
+
+
 # ------------------------------------------------------------------ step 6: sparse MLA
 
 @pytest.mark.parametrize("name", ALL)

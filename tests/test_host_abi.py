@@ -165,7 +165,9 @@ def test_refusals_return_codes_without_launching():
     assert L.dsa_index_scores(c, 1, 1, 8, 0, 1.0, odd, _FAKE, _FAKE, _FAKE, _FAKE, 0, _NULL,
                               _FAKE, _FAKE, _FAKE, _FAKE, _NULL) == -2
     # top-k rows beyond the register budget
-    assert L.dsa_topk_pools(c, 1, 65537, _FAKE, _FAKE, _FAKE, _NULL) == -14
+    assert L.dsa_topk_pools(c, 1, 65537, _FAKE, _FAKE, _FAKE, _NULL, 0, _NULL) == -14
+    # a workspace size without a pointer
+    assert L.dsa_topk_pools(c, 1, 16384, _FAKE, _FAKE, _FAKE, _NULL, 4096, _NULL) == -12
     # expand: more pools than the index_topk budget
     assert L.dsa_expand_selection(c, 1, 513, 1, 4096, 0, _FAKE, _FAKE, _FAKE, _FAKE, _FAKE,
                                   _NULL) == -2
