@@ -80,7 +80,7 @@ hipError_t launch_expand_selection(int Q, int Kw, int KP, int topk, int W, bool 
 
 // Sparse MLA split limits: token slots one block resolves up front, splits per row.
 constexpr int kMlaMaxSplit = 2048;
-constexpr int kMlaMaxSplits = 64;
+constexpr int kMlaMaxSplits = 16;
 static_assert(kMlaMaxSplit * kMlaMaxSplits >= DSA_MAX_MLA_WIDTH, "widest selection must fit");
 
 struct MlaPlan {

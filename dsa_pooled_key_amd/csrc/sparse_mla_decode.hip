@@ -638,11 +638,10 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(int H, int splits,
     auto o_vec = [&](int s) {
         return reinterpret_cast<const u32x4 *>(base + (size_t)s * kPartBytes + kPartHeader)[slot];
     };
-    // The first 16 splits' O vectors are fetched together with the headers: one round trip.
-    constexpr int kPre = 16;
-    u32x4 pre[kPre];
+    // Every split's O vectors are fetched together with the headers: one round trip.
+    u32x4 pre[kMaxSplits];
 #pragma unroll
-    for (int k = 0; k < kPre; ++k)
+    for (int k = 0; k < kMaxSplits; ++k)
         if (k < splits) pre[k] = o_vec(k);
     // Weights: thread (head h, quarter q) takes splits q, q+4, ...; the four quarters meet in LDS.
     {
@@ -698,17 +697,8 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(int H, int splits,
         }
     };
 #pragma unroll
-    for (int k = 0; k < kPre; ++k)
+    for (int k = 0; k < kMaxSplits; ++k)
         if (k < splits) accumulate(k, pre[k]);
-    for (int s0 = kPre; s0 < splits; s0 += 8) {  // more splits: eight loads in flight per thread
-        u32x4 val[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (s0 + k < splits) val[k] = o_vec(s0 + k);
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (s0 + k < splits) accumulate(s0 + k, val[k]);
-    }
     const int ch = 32 * z + (lane & 31);  // 128v + 32nt + (lane & 31)
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -744,8 +734,10 @@ hipError_t launch_v(const MlaPlan &plan, int Q, int W, int H, int B, float sm_sc
 }  // namespace
 
 // Split the token slots so that about 512 teams (two 4-wave teams per compute unit) run,
-// with at least 64 slots per split, at most kMaxSplit slots per split and at most
-// kMaxSplits splits; a row that already gives enough teams is not split. Where the teams fill
+// with at least 64 slots per split, at most kMaxSplit slots per split and at most kMaxSplits
+// (16) splits per row, so that the combine reads every partial in one round trip (a 2,048-slot
+// row in 32 splits of 64 took 1.5 us more, most of it in the combine); a row that already gives
+// enough teams is not split. Where the teams fill
 // one or two waves of resident blocks (512 to 1024 of them), pairs of splits share a block
 // (one partial per pair). Larger grids keep one team per block: two blocks on a compute unit
 // then drift apart in phase, so one's prologue overlaps the other's streaming, which paired
