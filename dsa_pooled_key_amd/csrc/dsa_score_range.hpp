@@ -10,10 +10,10 @@
 // pooled key is requested only for a slot that is valid and whose last token is at or before the
 // row position, so the keys of invalid pools are never read (the saving a compacted id list
 // exists for) and no id list is written or read. Every slot of the range is written by its lane:
-// the score and cand = 1 for a candidate, -inf and cand = 0 otherwise. Three dependent round
-// trips: the row's sequence and query; the flags; the keys. Dot products run on
-// v_mfma_f32_32x32x16_bf16 (heads as M, 32 pools as N); fp8 keys are converted to bf16 exactly
-// in registers; the relu-weighted head sum is the epilogue.
+// the score and cand = 1 for a candidate, -inf and cand = 0 otherwise. Two dependent round
+// trips once the row's sequence and position are known: the query with the flags; the keys.
+// Dot products run on v_mfma_f32_32x32x16_bf16 (heads as M, 32 pools as N); fp8 keys are
+// converted to bf16 exactly in registers; the relu-weighted head sum is the epilogue.
 #pragma once
 
 #include "dsa_device.hpp"
@@ -49,13 +49,12 @@ __device__ __forceinline__ float relu_weighted(const f32x16 &acc, const float (&
     return part;
 }
 
-// q_s: LDS of 32*D bf16 (16-byte aligned); w_s: LDS of 32 floats. Ends with the block's stores
-// issued (not waited for).
+// b, pos: row r's sequence and position. q_s: LDS of 32*D bf16 (16-byte aligned); w_s: LDS of
+// 32 floats. Ends with the block's stores issued (not waited for).
 template <int D, bool FP8, int TPW, int NT>
 __device__ __forceinline__ void score_range(
-    int r, int slot0, int B, int P, int Hi, int KP, int first_key, float scale,
-    const uint16_t *__restrict__ q, const float *__restrict__ w, const int32_t *__restrict__ row_seq,
-    const int32_t *__restrict__ row_pos, const void *__restrict__ keys,
+    int r, int b, long long pos, int slot0, int B, int P, int Hi, int KP, int first_key, float scale,
+    const uint16_t *__restrict__ q, const float *__restrict__ w, const void *__restrict__ keys,
     const float *__restrict__ key_scales, const uint8_t *__restrict__ pool_valid,
     float *__restrict__ scores, uint8_t *__restrict__ cand, uint16_t *q_s, float *w_s) {
     constexpr int kSteps = D / 16;
@@ -70,9 +69,8 @@ __device__ __forceinline__ void score_range(
     float *srow = scores + (size_t)r * P;
     uint8_t *crow = cand + (size_t)r * P;
 
-    // Round trip 1: the row's sequence and position, its query and head weights.
-    const int b = row_seq[r];
-    const long long pos = row_pos[r];
+    // Round trip 1: the row's query and head weights (its sequence b and position pos are
+    // the caller's), and with them the flags below.
     u32x4 qv[(kQVec + NT - 1) / NT];
 #pragma unroll
     for (int k = 0; k < (kQVec + NT - 1) / NT; ++k) {
@@ -82,10 +80,9 @@ __device__ __forceinline__ void score_range(
         if (e < 32 * D && h < Hi) qv[k] = *reinterpret_cast<const u32x4 *>(q + ((size_t)r * Hi) * D + e);
     }
     const float wv = tid < 32 && tid < Hi ? w[(size_t)r * Hi + tid] : 0.0f;
-    const bool row_ok = b >= 0 && b < B;
     const long long lim = row_pool_limit(b, pos, B, P, KP, first_key);
 
-    // Round trip 2: the validity flags of this lane's slots; round trip 3: their keys. The
+    // The validity flags of this lane's slots, then (round trip 2) their keys. The
     // flags sit under one branch that is uniform over the wave (a lane past the row's limit
     // reads the last flag in range and drops it), so they are requested together: under a
     // branch per tile the compiler waits for each flag before requesting the next.

@@ -206,15 +206,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     __shared__ float w_s[32];
     __shared__ int scan_s[kThreads / kWave + 1];
     __shared__ int item_s[2];
+    __shared__ int seq_s[kThreads];
+    __shared__ long long pos_s[kThreads];
     const int Q = gridDim.x, chunks = gridDim.y;
     int r = blockIdx.x, c = blockIdx.y;
+    int b;
+    long long pos;
     if (Q <= kThreads && Q * chunks < (1 << 15)) {
         const int t = threadIdx.x;
         const int L = blockIdx.y * Q + blockIdx.x;
         if (t == 0) item_s[0] = r, item_s[1] = c;  // (ordered before the finder by the scan)
         int act = 0;  // ranges of row t holding candidates
         if (t < Q) {
-            const long long lim = row_pool_limit(row_seq[t], row_pos[t], B, P, KP, first_key);
+            const int bt = row_seq[t];
+            const long long pt = row_pos[t];
+            seq_s[t] = bt;  // every row's geometry stays in LDS for the block's own row
+            pos_s[t] = pt;
+            const long long lim = row_pool_limit(bt, pt, B, P, KP, first_key);
             act = (int)((lim + kChunkV - 1) / kChunkV);
         }
         const int idle = t < Q ? chunks - act : 0;
@@ -231,10 +239,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         __syncthreads();
         r = min(max(item_s[0], 0), Q - 1);
         c = min(max(item_s[1], 0), chunks - 1);
+        b = seq_s[r];
+        pos = pos_s[r];
+    } else {
+        b = row_seq[r];
+        pos = row_pos[r];
     }
-    score_range<D, FP8, TPW, kThreads>(r, c * kChunkV, B, P, Hi, KP, first_key, scale, q, w,
-                                       row_seq, row_pos, keys, key_scales, pool_valid, scores,
-                                       cand, q_s, w_s);
+    score_range<D, FP8, TPW, kThreads>(r, b, pos, c * kChunkV, B, P, Hi, KP, first_key, scale, q,
+                                       w, keys, key_scales, pool_valid, scores, cand, q_s, w_s);
 }
 
 // Rows that all read one sequence's keys (prefill: consecutive positions of one sequence), as
