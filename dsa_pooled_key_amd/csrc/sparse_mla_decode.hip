@@ -416,18 +416,27 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
     };
 
     if constexpr (FP8) {
-        // Software-pipelined: the products of tile t-1 and the scores of tile t are independent
-        // and interleave in one instruction stream. Iteration t first refills the stage of tile
-        // t-2 (its products ended before barrier B of tile t-1) with tile t+2. Per tile two
-        // barriers: B (maxima exchanged; every wave past the products of t-1) and C (P of tile
-        // t visible, tile t+1 resident). P, alpha and the flags of tile t are read by the
-        // products of tile t in the next iteration, before barrier B rewrites them.
-        auto finish_tile = [&](int t, const float (&x)[4], const float (&sc)[4]) {  // t >= 1
-            lds_barrier();  // B
-            softmax(t, x, sc);
-            if (t + 2 < n_tiles) wait_vm<G_::kLoadsT>();  // tile t+1 landed, t+2 may fly
-            else wait_vm<0>();
-            lds_barrier();  // C
+        // Software-pipelined: the scores of tile t and the products of tile t-1 interleave.
+        // Iteration t first refills the stage of tile t-2 (its products ended before barrier C
+        // of tile t-1) with tile t+2. Per tile two barriers: B (maxima exchanged) and C (P of
+        // tile t visible, tile t+1 resident). Before B a wave takes its P operand of tile t-1
+        // into registers and applies tile t-1's rescale, then scores tile t; after B the
+        // products of tile t-1 run beside the softmax of tile t, whose P, alpha and flag
+        // writes therefore touch nothing those products still read.
+        auto pv = [&](int t, const u32x4 (&pa)[2]) {  // O += P(t) V(t), P already in registers
+            const uint8_t *TP = ring + (t % NS) * G_::kTileBytes;
+            u32x2 vr[2][4];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) vr[ks][nt] = lds_read_tr8(TP + v_off[ks][nt]);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        as_bf16x8(pa[ks]), as_bf16x8(e4m3x8_to_bf16x8(vr[ks][nt].x, vr[ks][nt].y)),
+                        acc[nt], 0, 0, 0);
         };
         if (n_iter > 0) {
             float x[4], sc[4];
@@ -441,45 +450,27 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
             }
             lds_barrier();  // C
         }
-        // Iteration t: every LDS operand of the refill, of the products of tile t-1 and of the
+        // Iteration t, before B: every LDS operand of the refill, of tile t-1's P and of the
         // scores of tile t is requested before the first is used, so their latencies overlap
         // one another and the MFMA work instead of adding up.
-        auto step = [&](int t, float (&x)[4], float (&sc)[4]) {
+        auto step = [&](int t, float (&x)[4], float (&sc)[4], u32x4 (&pa)[2]) {
             const bool refill = t + 2 < n_tiles;
-            const uint8_t *TP = ring + ((t - 1) % NS) * G_::kTileBytes;
             const uint8_t *TS = ring + (t % NS) * G_::kTileBytes;
             TileRows nr{};
             if (refill) nr = read_rows(t + 2);
             const int resc = rescale_s[(t - 1) & 1];
-            u32x4 pa[2];
-            u32x2 vr[2][4];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
+            for (int ks = 0; ks < 2; ++ks)
                 pa[ks] = *reinterpret_cast<const u32x4 *>(pl + (lane & 31) * kPStride + 16 * ks +
                                                           (lane >> 5) * 8);
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt) vr[ks][nt] = lds_read_tr8(TP + v_off[ks][nt]);
-            }
             u32x4 kr[8];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) kr[jj] = lds_load<u32x4>(TS, qk_off[jj]);
+            for (int jj = 0; jj < 8; ++jj) kr[jj] = lds_load<u32x4>(TS, qk_off[jj & 3] + 256 * (jj >> 2));
             const int4 rw = score_rows(t);
             const f32x4 sv = score_scales(t);
             __builtin_amdgcn_sched_barrier(0);
             if (refill) issue_rows(t + 2, nr);
             if (resc) rescale_acc();
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
-                    acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        as_bf16x8(pa[ks]), as_bf16x8(e4m3x8_to_bf16x8(vr[ks][nt].x, vr[ks][nt].y)),
-                        acc[nt], 0, 0, 0);
-            // The second half of the key chunks takes the registers the V fragments held.
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int jj = 4; jj < 8; ++jj) kr[jj] = lds_load<u32x4>(TS, qk_off[jj & 3] + 256);
-            __builtin_amdgcn_sched_barrier(0);
             f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
@@ -493,8 +484,14 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
         for (int t = 1; t < n_iter; ++t) {
             float x[4], sc[4];
             if (t < n_tiles) {
-                step(t, x, sc);
-                finish_tile(t, x, sc);
+                u32x4 pa[2];
+                step(t, x, sc, pa);
+                lds_barrier();  // B
+                softmax(t, x, sc);
+                pv(t - 1, pa);
+                if (t + 2 < n_tiles) wait_vm<G_::kLoadsT>();  // tile t+1 landed, t+2 may fly
+                else wait_vm<0>();
+                lds_barrier();  // C
             } else {
                 if (t == n_tiles) products(t - 1);  // the team's last tile
                 lds_barrier();  // B
