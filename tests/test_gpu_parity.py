@@ -389,6 +389,39 @@ def test_sparse_mla_paired_splits(name, n_rows):
     assert np.all(np.isneginf(lse.cpu().numpy()[0]))
 
 
+@pytest.mark.parametrize("Q,fp8", [(1, False), (64, False), (64, True)])
+def test_sparse_mla_widest_selection(Q, fp8):
+    """The widest selection the boundary takes (32,768 token slots: 16 splits of 2,048, the
+    most the combine merges), on one row (16 one-team splits) and on 64 rows (1,024 teams, so
+    two 2,048-slot splits share each block); random tokens of one 40,000-token sequence with
+    scattered -1 slots; the last row against the oracle."""
+    S, W, H = 40000, 32768, 32
+    rng = np.random.default_rng(31 + Q + fp8)
+    kvf = rng.normal(0.0, 0.5, (S, 512)).astype(np.float32)
+    scales = None
+    if fp8:
+        kv, scales = synth.e4m3_quantize_rows(kvf)
+        kv_d = torch.from_numpy(kv).cuda()
+        sc_d = _dev(scales)
+    else:
+        kv = synth.bf16_bits(kvf)
+        kv_d = torch.from_numpy(kv.view(np.int16)).cuda().view(torch.bfloat16)
+        sc_d = None
+    q = synth.bf16_bits(rng.normal(0.0, 1.0, (Q, H, 512)).astype(np.float32))
+    tok = np.stack([rng.permutation(S)[:W] for _ in range(Q)]).astype(np.int32)
+    tok[rng.random(tok.shape) < 0.01] = -1
+    rs = np.zeros(Q, np.int32)
+    cfg = dsa.Config.make(index_heads=32, index_head_dim=128, index_kpool=4, index_topk=W, heads=H)
+    qd = torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16)
+    sm = 1.0 / np.sqrt(576.0)
+    out, lse = dsa.sparse_mla_decode(cfg, qd, _dev(tok), _dev(rs), kv_d, B=1, sm_scale=sm, S=S,
+                                     kv_scales=sc_d)
+    rows = np.array([Q - 1])
+    ro, rl = oracle.sparse_mla(q[rows], tok[rows], rs[rows], kv, sm_scale=sm, S=S,
+                               kv_scales=scales)
+    _check_mla(out.cpu().numpy()[rows], lse.cpu().numpy()[rows], ro, rl, fp8)
+
+
 def test_sparse_mla_repeatable_paging_invariant_and_masks_bad_ids():
     di, x, _, _ = case("ragged_bf16")
     wl = di.wl
