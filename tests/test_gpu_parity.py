@@ -310,6 +310,33 @@ def test_topk_ties_signs_and_row_lengths(P, kw, seed):
     assert np.array_equal(ftok.cpu().numpy(), tok_ref)
 
 
+@pytest.mark.parametrize("P,kw,seed", [(8192, 512, 40), (16384, 512, 41), (16384, 100, 42),
+                                       (32768, 512, 43), (32768, 2048, 44)])
+def test_topk_rows_of_many_candidates_a_thread(P, kw, seed):
+    """One block a row with at least 8 pools a thread and four times kw candidates or more:
+    rows whose candidates sit in fewer than kw threads, ascending and descending scores, ties
+    at the cutoff across many threads, one huge outlier, sparse candidates and plain normal
+    scores."""
+    rng = np.random.default_rng(seed)
+    Q = 8
+    scores = rng.standard_normal((Q, P)).astype(np.float32)
+    cand = np.ones((Q, P), np.uint8)
+    cand[0] = 0
+    cand[0, : 4 * kw + 16] = 1                                         # few threads hold them
+    scores[1] = np.linspace(-3.0, 3.0, P, dtype=np.float32)            # ascending
+    scores[2] = np.linspace(3.0, -3.0, P, dtype=np.float32)            # descending
+    scores[3] = (rng.integers(0, 4, P) / 2.0).astype(np.float32)       # ties at the cutoff
+    scores[4, rng.integers(0, P)] = 1.0e30                             # one outlier
+    scores[5] = np.where(rng.random(P) < 0.5, 2.0, scores[5]).astype(np.float32)
+    cand[6] = (rng.random(P) < 0.3).astype(np.uint8)                   # sparse candidates
+    scores[cand == 0] = -np.inf
+    cfg = dsa.Config.make(index_heads=32, index_head_dim=128, index_kpool=1, index_topk=kw,
+                          heads=32)
+    got = dsa.topk_pools(cfg, _dev(scores), _dev(cand), ws=False).cpu().numpy()
+    ref = oracle.topk_pools(scores, cand, min(kw, P))
+    assert np.array_equal(got, ref)
+
+
 @pytest.mark.parametrize("P,kw,seed", [(16385, 512, 20), (24577, 512, 21), (32768, 512, 22),
                                        (65536, 512, 23), (40000, 100, 24), (32768, 2048, 25)])
 def test_topk_two_stage_equals_one_block(P, kw, seed):
