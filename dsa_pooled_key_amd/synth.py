@@ -18,6 +18,7 @@ size):
 * ``decode_b8_128k``  8 queries, every sequence at 131,072 tokens, otherwise decode_b8_32k.
 * ``fp8_mixed_b32``   32 queries, log-uniform lengths in [4K, 131,072], kpool 8, topk 4,096,
   fp8 pooled keys and fp8 paged latent with per-row f32 scales, ~5% of slots invalid.
+* ``fp8_mixed_b128``  fp8_mixed_b32's recipe with 128 queries (batch scaling).
 
 Every workload also has an exact twin (``exact=True``): the same shapes with small dyadic
 values (q, keys in multiples of 1/4 .. 1/32, w in multiples of 1/8, scale 2^-3, power-of-two
@@ -193,6 +194,11 @@ WORKLOADS = {
     "fp8_mixed_b32": Workload("fp8_mixed_b32", B=32, S=131072, Q=32, kpool=8, topk=4096,
                               index_heads=32, index_dim=128, heads=32, key_fp8=True,
                               kv_fp8=True, paged=True, lengths="loguniform", invalid_rate=0.05),
+    # fp8_mixed_b32's recipe at 4x the batch (a batch-scaling line of the benchmark: the
+    # same kernels with their fixed per-launch latency spread over more rows).
+    "fp8_mixed_b128": Workload("fp8_mixed_b128", B=128, S=131072, Q=128, kpool=8, topk=4096,
+                               index_heads=32, index_dim=128, heads=32, key_fp8=True,
+                               kv_fp8=True, paged=True, lengths="loguniform", invalid_rate=0.05),
     # Small ragged workloads for parity at oracle-friendly sizes: sizes that are not multiples
     # of any tile, first_key > 0, tail slots, head counts below and above 32.
     "ragged_bf16": Workload("ragged_bf16", B=3, S=4999, Q=3, kpool=4, topk=200, index_heads=20,

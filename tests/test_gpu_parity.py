@@ -25,6 +25,9 @@ pytestmark = pytest.mark.gpu
 SMALL = ["tiny", "ragged_bf16", "ragged_fp8", "ragged_prefill"]
 FULL = ["decode_b8_32k", "decode_b4_256k", "prefill_2048_64k", "fp8_mixed_b32"]
 ALL = SMALL + FULL
+# The batch-scaling workload (fp8_mixed_b32's recipe at 128 rows): the decode chain's
+# launches on it, rows sampled.
+SCALE = ["fp8_mixed_b128"]
 
 _CACHE = {}
 
@@ -142,7 +145,7 @@ def _compact_index(di, x, pool_valid=None, row_seq=None, row_pos=None):
         scale=di.scale, key_scales=x.key_scales)
 
 
-@pytest.mark.parametrize("name", ALL)
+@pytest.mark.parametrize("name", ALL + SCALE)
 def test_compact_index_scores(name):
     di, x, ids, nv = case(name)
     scores, cand = _compact_index(di, x)
@@ -256,7 +259,7 @@ def test_compact_index_scores_edge_rows():
 
 # ------------------------------------------------------------------ steps 4 and 5
 
-@pytest.mark.parametrize("name", ALL)
+@pytest.mark.parametrize("name", ALL + SCALE)
 def test_topk_and_expand_bit_exact_on_oracle_scores(name):
     di, x, ids, nv = case(name)
     wl = di.wl
@@ -368,7 +371,7 @@ def test_topk_two_stage_equals_one_block(P, kw, seed):
 
 # ------------------------------------------------------------------ step 6: sparse MLA
 
-@pytest.mark.parametrize("name", ALL)
+@pytest.mark.parametrize("name", ALL + SCALE)
 def test_sparse_mla_decode(name):
     di, x, _, _ = case(name)
     wl = di.wl
@@ -849,7 +852,7 @@ def test_fused_and_separate_selection_agree(name):
     assert np.array_equal(a.token_ids.cpu().numpy(), b.token_ids.cpu().numpy())
 
 
-@pytest.mark.parametrize("name", ALL)
+@pytest.mark.parametrize("name", ALL + SCALE)
 def test_selection_chain_general_differs_only_at_the_cutoff(name):
     di, x, ids, nv = case(name)
     step = DecodeStep(di.wl, x, di.scale, di.sm_scale)
