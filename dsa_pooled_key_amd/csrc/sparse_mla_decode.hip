@@ -141,20 +141,25 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
     // The block's 32 query rows (1 KiB each) are staged once through LDS, in the upper half of
     // team 0's ring, which no tile uses before every wave of the block has taken its fragment:
     // wave w of the block fetches 8/TEAMS heads from (8/TEAMS)w on, chunk c of head row h at
-    // position c ^ swz<false>(h).
+    // position c ^ swz<false>(h). fp8 issues the copies with tile 0's, after the token ids and
+    // table entries have landed, so those small loads do not queue behind them (47.3 against
+    // 47.7 us for the fp8_mixed_b32 step); bf16 issues them first (later, its X128 decode and
+    // prefill attention took 3% longer).
     uint8_t *const qlds = ring_all[0] + 32768;
     const int qk_head_local = 16 * (v & 1) + (lane & 15);
     const int qk_head = g * 32 + qk_head_local;
     constexpr int kQHeads = 8 / TEAMS;
+    auto stage_q = [&]() {
 #pragma unroll
-    for (int k = 0; k < kQHeads; ++k) {
-        const int hl = kQHeads * (int)(threadIdx.x / kWave) + k;
-        if (g * 32 + hl < H)
-            dma16(reinterpret_cast<const uint8_t *>(q_abs + ((size_t)r * H + g * 32 + hl) * kC) +
-                      16 * (lane ^ swz<false>(hl)),
-                  __builtin_amdgcn_readfirstlane(lds_offset(qlds + hl * 1024)));
-    }
-
+        for (int k = 0; k < kQHeads; ++k) {
+            const int hl = kQHeads * (int)(threadIdx.x / kWave) + k;
+            if (g * 32 + hl < H)
+                dma16(reinterpret_cast<const uint8_t *>(q_abs + ((size_t)r * H + g * 32 + hl) * kC) +
+                          16 * (lane ^ swz<false>(hl)),
+                      __builtin_amdgcn_readfirstlane(lds_offset(qlds + hl * 1024)));
+        }
+    };
+    if constexpr (!FP8) stage_q();
     // ---- DMA: wave v fetches rows 8v..8v+7 of every tile (and, for fp8, their scales). A slot
     // without a token fetches latent row 0 (finite data; its weight is zero).
     const int dma_rl = lane / G_::kLanesPerRow;                    // row within one load
@@ -225,6 +230,7 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
     // the chip-wide burst of first tiles each team's tile 0 then lands before any tile 1
     // (fp8 issues tile 1 after the prologue barrier, 29.9 against 30.3 us for the stage on
     // fp8_mixed_b32).
+    if constexpr (FP8) stage_q();  // the query rows with tile 0
     const int pre = kv_rows > 0 ? min(n_ptiles, 1) : 0;
     for (int t = 0; t < pre; ++t) issue(t);
     my_last = (int)wave_reduce_u32((uint32_t)my_last,
