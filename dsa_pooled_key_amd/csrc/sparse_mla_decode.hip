@@ -630,44 +630,48 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
 // 128v + 32nt .. +31 of all 32 heads. Per head the splits' (max m_s, sum l_s) give
 // M = max m_s, L = sum l_s e^(m_s - M) and the weights e^(m_s - M) / L; out = sum_s weight_s O_s,
 // lse = M + log L. Splits without tokens (l_s = 0) get weight 0; their O is zero.
-__global__ __launch_bounds__(128) void mla_combine_kernel(int H, int splits,
-                                                          const uint8_t *__restrict__ ws,
+// NP (2..kMaxSplits) is the split count, a template parameter so that every load count is
+// known at compile time.
+template <int NP>
+__global__ __launch_bounds__(128) void mla_combine_kernel(const int H, const uint8_t *__restrict__ ws,
                                                           float *__restrict__ out,
                                                           float *__restrict__ lse) {
-    __shared__ __attribute__((aligned(16))) float wgt[kMaxSplits][32];
+    __shared__ __attribute__((aligned(16))) float wgt[NP][32];
     __shared__ float red4[4][32];
     const int r = blockIdx.x;
     const int g = blockIdx.y;
     const int G = gridDim.y;
     const int z = blockIdx.z;  // 4v + nt
     const int tid = threadIdx.x;
-    const uint8_t *base = ws + ((size_t)r * G + g) * splits * kPartBytes;
+    const uint8_t *base = ws + ((size_t)r * G + g) * NP * kPartBytes;
     const int i8 = tid >> 6, lane = tid & 63;
     const int slot = (z * 2 + i8) * kWave + lane;   // 16-byte vector within O
     auto o_vec = [&](int s) {
         return reinterpret_cast<const u32x4 *>(base + (size_t)s * kPartBytes + kPartHeader)[slot];
     };
-    // Every split's O vectors are fetched together with the headers: one round trip.
-    u32x4 pre[kMaxSplits];
-#pragma unroll
-    for (int k = 0; k < kMaxSplits; ++k)
-        if (k < splits) pre[k] = o_vec(k);
+    // Every split's header and O vectors are fetched in one round trip, the headers first: with
+    // the split count fixed at compile time the weights below wait only for the headers
+    // (loads complete in order) while the O vectors are still in flight.
     // Weights: thread (head h, quarter q) takes splits q, q+4, ...; the four quarters meet in LDS.
-    {
-        const int h = tid & 31, q = tid >> 5;
-        constexpr int kPer = kMaxSplits / 4;
-        float ms[kPer], ls[kPer];
+    const int h = tid & 31, q = tid >> 5;
+    constexpr int kPer = (NP + 3) / 4;
+    float ms[kPer], ls[kPer];
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int sp = q + 4 * j;
-            ms[j] = -INFINITY;
-            ls[j] = 0.0f;
-            if (sp < splits) {
-                const float *hd = reinterpret_cast<const float *>(base + (size_t)sp * kPartBytes);
-                ms[j] = hd[h];
-                ls[j] = hd[32 + h];
-            }
+    for (int j = 0; j < kPer; ++j) {
+        const int sp = q + 4 * j;
+        ms[j] = -INFINITY;
+        ls[j] = 0.0f;
+        if (sp < NP) {
+            const float *hd = reinterpret_cast<const float *>(base + (size_t)sp * kPartBytes);
+            ms[j] = hd[h];
+            ls[j] = hd[32 + h];
         }
+    }
+    u32x4 pre[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) pre[k] = o_vec(k);
+    __builtin_amdgcn_sched_barrier(0);  // every load issued before the first use of a header
+    {
         float M = -INFINITY;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) M = ls[j] > 0.0f ? fmaxf(M, ms[j]) : M;
@@ -687,7 +691,7 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(int H, int splits,
         const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
         for (int j = 0; j < kPer; ++j)
-            if (q + 4 * j < splits) wgt[q + 4 * j][h] = ms[j] * inv;
+            if (q + 4 * j < NP) wgt[q + 4 * j][h] = ms[j] * inv;
         if (lse != nullptr && z == 0 && q == 0 && g * 32 + h < H)
             lse[(size_t)r * H + g * 32 + h] = L > 0.0f ? M + logf(L) : -INFINITY;
     }
@@ -706,13 +710,25 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(int H, int splits,
         }
     };
 #pragma unroll
-    for (int k = 0; k < kMaxSplits; ++k)
-        if (k < splits) accumulate(k, pre[k]);
+    for (int k = 0; k < NP; ++k) accumulate(k, pre[k]);
     const int ch = 32 * z + (lane & 31);  // 128v + 32nt + (lane & 31)
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const int h = g * 32 + m_lo + (c & 3) + 8 * (c >> 2);
         if (h < H) out[((size_t)r * H + h) * kC + ch] = o[c];
+    }
+}
+
+template <int NP>
+hipError_t launch_combine(int parts, int Q, int groups, int H, const uint8_t *ws, float *out,
+                          float *lse, hipStream_t stream) {
+    if constexpr (NP > kMaxSplits) {
+        return hipErrorInvalidValue;
+    } else {
+        if (parts != NP) return launch_combine<NP + 1>(parts, Q, groups, H, ws, out, lse, stream);
+        hipLaunchKernelGGL(mla_combine_kernel<NP>, dim3(Q, groups, 16), dim3(128), 0, stream, H, ws,
+                           out, lse);
+        return hipGetLastError();
     }
 }
 
@@ -735,9 +751,8 @@ hipError_t launch_v(const MlaPlan &plan, int Q, int W, int H, int B, float sm_sc
                            static_cast<float *>(ws));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.parts == 1) return e;
-    hipLaunchKernelGGL(mla_combine_kernel, dim3(Q, plan.groups, 16), dim3(128), 0, stream, H, plan.parts,
-                       static_cast<const uint8_t *>(ws), out, lse);
-    return hipGetLastError();
+    return launch_combine<2>(plan.parts, Q, plan.groups, H, static_cast<const uint8_t *>(ws), out,
+                             lse, stream);
 }
 
 }  // namespace

@@ -419,6 +419,30 @@ def test_sparse_mla_paired_splits(name, n_rows):
     assert np.all(np.isneginf(lse.cpu().numpy()[0]))
 
 
+@pytest.mark.parametrize("n_splits", list(range(2, 17)))
+def test_sparse_mla_every_split_count(n_splits):
+    """Rows of 64 * n - 13 token slots are cut into n splits of 64 (two rows, one head group),
+    so the merge of the split partials runs with every split count it is built for (2..16);
+    against the oracle."""
+    S, H, Q = 2000, 32, 2
+    W = 64 * n_splits - 13
+    rng = np.random.default_rng(60 + n_splits)
+    kv = synth.bf16_bits(rng.normal(0.0, 0.5, (S, 512)).astype(np.float32))
+    q = synth.bf16_bits(rng.normal(0.0, 1.0, (Q, H, 512)).astype(np.float32))
+    tok = rng.integers(0, S, (Q, W)).astype(np.int32)
+    tok[rng.random(tok.shape) < 0.05] = -1
+    tok[1, 64:128] = -1                      # one split of row 1 without tokens
+    rs = np.zeros(Q, np.int32)
+    cfg = dsa.Config.make(index_heads=32, index_head_dim=128, index_kpool=1, index_topk=W, heads=H)
+    assert dsa.sparse_mla_workspace(cfg, Q, W) > 0
+    kv_d = torch.from_numpy(kv.view(np.int16)).cuda().view(torch.bfloat16)
+    qd = torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16)
+    sm = 1.0 / np.sqrt(576.0)
+    out, lse = dsa.sparse_mla_decode(cfg, qd, _dev(tok), _dev(rs), kv_d, B=1, sm_scale=sm, S=S)
+    ro, rl = oracle.sparse_mla(q, tok, rs, kv, sm_scale=sm, S=S)
+    _check_mla(out.cpu().numpy(), lse.cpu().numpy(), ro, rl, False)
+
+
 @pytest.mark.parametrize("Q,fp8", [(1, False), (64, False), (64, True)])
 def test_sparse_mla_widest_selection(Q, fp8):
     """The widest selection the boundary takes (32,768 token slots: 16 splits of 2,048, the
