@@ -194,6 +194,23 @@ def test_refusals_return_codes_without_launching():
     assert L.dsa_compact_pools(0, 8, _NULL, _NULL, _NULL, _NULL) == 0
 
 
+def test_sparse_mla_workspace_never_needs_more_than_sixteen_partials():
+    """The split merge is built for 2 to 16 partials per (row, head group): the workspace the
+    library asks for (one 33,024-byte partial per part) stays within that for every width up
+    to the widest selection the boundary takes, from one row to prefill-sized batches."""
+    L = dsa.lib()
+    part = 256 + 32 * 512 * 2
+    for heads in (32, 40):
+        c = ctypes.byref(_cfg(heads=heads))
+        groups = (heads + 31) // 32
+        for Q in (1, 2, 8, 32, 64, 128, 256, 2048):
+            for W in (1, 63, 64, 65, 1000, 2048, 4096, 4103, 16384, 32767, 32768):
+                ws = L.dsa_sparse_mla_decode_workspace(c, Q, W)
+                assert ws % (Q * groups * part) == 0
+                parts = ws // (Q * groups * part)
+                assert parts == 0 or 2 <= parts <= 16, (heads, Q, W, parts)
+
+
 def test_refusals_of_the_fp8_writers_upkeep_and_masked_check():
     """Refused before any launch (no GPU needed): shapes the kernels are not built for, null
     buffers, bad dtypes, negative sizes."""
