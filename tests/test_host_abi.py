@@ -243,3 +243,17 @@ def test_refusals_of_the_fp8_writers_upkeep_and_masked_check():
     assert L.dsa_mla_masked_attn(c, 1, 64, 1, ctypes.c_float(0.0625), _FAKE, _FAKE, _FAKE, _FAKE,
                                  2, _NULL, 64, _NULL, 0, 64, _FAKE, _NULL, _NULL) == -1
     assert L.dsa_topk_to_mask(1, 4, 64, _FAKE, _NULL, _NULL) == -1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it prints why and exits with status 2, before
+    it touches a device."""
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=300, cwd=root)
+    assert res.returncode == 2
+    line = json.loads(res.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
