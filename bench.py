@@ -446,7 +446,7 @@ def run_cpu_baseline(di, sample_every: int, min_seconds: float = 10.0, max_passe
         if dt >= min_seconds or passes >= max_passes:
             break
     return {"value": passes * len(rows) / dt, "unit": "queries/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "kind": "oracle",
             "sample": f"{len(rows)} of the {wl.Q} queries of one step (every {sample_every}th), "
                       f"whole decode chain, {passes} passes, {dt:.1f} s wall"}
 

@@ -37,7 +37,7 @@ EXPORTED = [
     "dsa_topk_to_mask", "dsa_mla_masked_attn",
     "dsa_compact_pools", "dsa_index_scores",
     "dsa_compact_index_scores",
-    "dsa_topk_workspace", "dsa_topk_pools", "dsa_expand_selection", "dsa_topk_expand",
+    "dsa_topk_workspace", "dsa_topk_pools_workspace", "dsa_topk_pools", "dsa_expand_selection", "dsa_topk_expand",
     "dsa_sparse_mla_decode_workspace",
     "dsa_sparse_mla_decode", "dsa_absorb_q", "dsa_absorb_o", "dsa_f32_to_bf16_rne",
 ]
@@ -101,6 +101,7 @@ def lib():
             "dsa_compact_index_scores": ([_CFG, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P,
                                           _P, _P, _P, _P], _I),
             "dsa_topk_workspace": ([_CFG, _I, _I], _SZ),
+            "dsa_topk_pools_workspace": ([_CFG, _I, _I], _SZ),
             "dsa_topk_pools": ([_CFG, _I, _I, _P, _P, _P, _P, _SZ, _P], _I),
             "dsa_expand_selection": ([_CFG, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P], _I),
             "dsa_topk_expand": ([_CFG, _I, _I, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _SZ,
@@ -492,10 +493,11 @@ def sparse_mla_workspace(cfg: Config, Q: int, W: int) -> int:
 
 
 def sparse_mla_decode(cfg: Config, q_abs, token_ids, row_seq, kv, *, B: int, sm_scale: float,
-                      S: int = 0, kv_scales=None, block_table=None, block_size: int = 64,
+                      S: int, kv_scales=None, block_table=None, block_size: int = 64,
                       out=None, lse=None, ws=None):
     """q_abs [Q,H,512] bf16; token_ids [Q,W] i32; kv [rows,512] bf16 or fp8 (+ kv_scales
-    [rows] f32); contiguous rows b*S + t, or paged through block_table [B, max_blocks].
+    [rows] f32); contiguous rows b*S + t (S > 0 required), or paged through block_table
+    [B, max_blocks] (S > 0 also bounds the token ids; 0 = no bound).
     Returns (out [Q,H,512] f32, lse [Q,H] f32)."""
     _dev(q_abs, "q_abs", (torch.bfloat16,))
     Q, H, C = q_abs.shape

@@ -379,6 +379,10 @@ size_t dsa_topk_workspace(const dsa_config *cfg, int Q, int P) {
     return dsa::topk_workspace_bytes(Q, P, (int)select_k(cfg, P));
 }
 
+size_t dsa_topk_pools_workspace(const dsa_config *cfg, int Q, int P) {
+    return dsa_topk_workspace(cfg, Q, P);
+}
+
 int dsa_topk_pools(const dsa_config *cfg, int Q, int P, const float *scores, const uint8_t *cand,
                    int32_t *sel, void *ws, size_t ws_bytes, hipStream_t stream) {
     clear_error();
@@ -479,6 +483,10 @@ int dsa_sparse_mla_decode(const dsa_config *cfg, int Q, int W, int B, float sm_s
     if (block_table) {
         if (block_size <= 0 || max_blocks < 0)
             return set_error(DSA_ERR_BAD_SIZE, "sparse_mla_decode: paged latent needs block_size > 0");
+    } else if (S <= 0 && W > 0) {
+        // Contiguous rows are b*S + t: without a positive stride every sequence would read
+        // sequence 0's rows.
+        return set_error(DSA_ERR_BAD_SIZE, "sparse_mla_decode: a contiguous latent needs S > 0");
     }
     if (!aligned(q_abs, 16) || (kv && !aligned(kv, 16)) || !aligned(out, 16))
         return set_error(DSA_ERR_BAD_SIZE, "sparse_mla_decode: q_abs, kv and out need 16-byte alignment");

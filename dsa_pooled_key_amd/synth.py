@@ -216,6 +216,13 @@ WORKLOADS = {
 # is 256 on GLM-5.3, so 1/16). The exact twins use 2^-3 for the index scale.
 SM_SCALE = 1.0 / 16.0
 
+# The "peaked" variant of a workload draws q_abs with this standard deviation instead of 0.5.
+# A logit is SM_SCALE * sum_c q_c v_c over 512 channels with latent values of standard
+# deviation 0.5, so its standard deviation is 16^-1 * sqrt(512) * 0.5 * std(q) = std(q)/sqrt(2);
+# 3 * sqrt(2) gives logits of standard deviation 3, and a softmax over a few thousand tokens
+# then puts most of its weight on a few dozen of them (at std 0.5 it is nearly uniform).
+PEAKED_QABS_STD = 3.0 * math.sqrt(2.0)
+
 
 def index_scale(wl: Workload, exact: bool) -> float:
     return 0.125 if exact else float(np.float32(wl.index_dim ** -0.5))
@@ -368,7 +375,22 @@ def _layout_kv(wl: Workload, L: np.ndarray, rng_perm):
     return total * BLOCK, table
 
 
-def make_decode_inputs(name: str, seed: int = 0, exact: bool = False) -> DecodeInputs:
+def _q_abs(wl: Workload, ss, exact: bool, peaked: bool) -> np.ndarray:
+    shape = (wl.Q, wl.heads, LATENT)
+    if exact:
+        return bf16_bits(_dyadic(ss, shape, 4, 4))
+    return bf16_bits(_normal(ss, shape, PEAKED_QABS_STD if peaked else 0.5))
+
+
+def peaked_q_abs(name: str, seed: int = 0) -> np.ndarray:
+    """The q_abs of make_decode_inputs(name, seed, peaked=True), drawn alone."""
+    return _q_abs(WORKLOADS[name], _streams(seed, 11)[6], False, True)
+
+
+def make_decode_inputs(name: str, seed: int = 0, exact: bool = False,
+                       peaked: bool = False) -> DecodeInputs:
+    """The workload's decode inputs. ``peaked`` draws q_abs with PEAKED_QABS_STD (general
+    inputs only); every other tensor is the same as without it."""
     wl = WORKLOADS[name]
     (s_len, s_valid, s_keys, s_kscale, s_q, s_w, s_qabs, s_kv, s_kvscale,
      s_perm, s_rows) = _streams(seed, 11)
@@ -407,10 +429,7 @@ def make_decode_inputs(name: str, seed: int = 0, exact: bool = False) -> DecodeI
     row_seq, row_pos = query_rows(wl, L, _rng(s_rows))
 
     # latent side
-    if exact:
-        q_abs = bf16_bits(_dyadic(s_qabs, (Q, H, LATENT), 4, 4))
-    else:
-        q_abs = bf16_bits(_normal(s_qabs, (Q, H, LATENT), 0.5))
+    q_abs = _q_abs(wl, s_qabs, exact, peaked)
     rows, table = _layout_kv(wl, L, _rng(s_perm))
     kv_scales = None
     if wl.kv_fp8:
@@ -448,7 +467,8 @@ def make_kpool_inputs(name: str, seed: int = 0, exact: bool = False,
     make_decode_inputs with the same seed). ``batch`` keeps only the first sequences.
     The exact twin has keys in multiples of 1/4, gate 0, and ape either 0 (uniform pool
     weights, kpool 4) or +-64 on one slot per channel (one-hot weights, kpool 8), so pooled
-    keys are exact in bf16 and in e4m3."""
+    keys are exact in bf16 and in e4m3; with fp8 pooled keys, channel 0 is +-7/4 on every
+    token, which makes the per-row fp8 scale a power of two."""
     wl = WORKLOADS[name]
     s_len, s_valid = _streams(seed, 11)[:2]          # the decode inputs' lengths and masks
     (s_k, s_gate, s_ape, s_hot) = _streams(seed + 1000, 4)
@@ -458,7 +478,14 @@ def make_kpool_inputs(name: str, seed: int = 0, exact: bool = False,
     valid = np.ascontiguousarray(valid[:B])
     shape = (B, wl.S, wl.index_dim)
     if exact:
-        k = bf16_bits(_dyadic(s_k, shape, 4, 4))
+        kf = _dyadic(s_k, shape, 4, 4)
+        if wl.key_fp8:
+            # Channel 0 of every token key is +-7/4, so every one-hot pooled row has
+            # amax 7/4 and the stored scale amax/448 is 2^-8; each value (a multiple of 1/4 of
+            # magnitude at most 7/4) times 256 is then an e4m3 value, and the fp8 keys, their
+            # scales and the scores computed from them are all exact.
+            kf[..., 0] = np.where(kf[..., 0] < 0, np.float32(-1.75), np.float32(1.75))
+        k = bf16_bits(kf)
         gate = np.zeros(shape, np.uint16)
         if wl.kpool == 8:
             hot = _rng(s_hot).integers(0, wl.kpool, size=wl.index_dim)

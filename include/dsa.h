@@ -241,11 +241,13 @@ int dsa_compact_index_scores(const dsa_config *cfg, int Q, int B, int P, int fir
  * shows is needed for a stable selection. Kw = dsa_select_k(cfg, P).
  * scores: [Q, P] f32; cand: [Q, P] u8; sel: [Q, Kw] i32. Scores must not be NaN.
  * ws: device workspace of dsa_topk_workspace(cfg, Q, P) bytes (16-byte aligned), or NULL with
- * ws_bytes 0. Given it, few long rows (at most 64 rows of several 4,096-pool segments) are
+ * ws_bytes 0. Given it, few long rows (at most 64 rows of several 8,192-pool segments) are
  * selected in two launches: each segment's best Kw first (one block per row and segment),
  * then the row's best Kw among those; without it, or when too small, one block per row selects
  * from the whole row. Both give the same sel. */
 size_t dsa_topk_workspace(const dsa_config *cfg, int Q, int P);
+/* Alias of dsa_topk_workspace named after dsa_topk_pools: identical result. */
+size_t dsa_topk_pools_workspace(const dsa_config *cfg, int Q, int P);
 int dsa_topk_pools(const dsa_config *cfg, int Q, int P, const float *scores, const uint8_t *cand,
                    int32_t *sel, void *ws, size_t ws_bytes, hipStream_t stream);
 
@@ -284,7 +286,8 @@ int dsa_topk_expand(const dsa_config *cfg, int Q, int P, const float *scores, co
  * row is e4m3 * scale), else NULL. Row of token t: contiguous (block_table == NULL)
  * b*S + t; paged: block_table[b*max_blocks + t/block_size]*block_size + t%block_size with
  * block_table [B, max_blocks] i32. Token ids at or past S (when S > 0), blocks mapped to a
- * negative entry, and rows outside [0, kv_rows) are skipped like -1.
+ * negative entry, and rows outside [0, kv_rows) are skipped like -1. A contiguous latent
+ * needs S > 0 (DSA_ERR_BAD_SIZE otherwise, when W > 0); paged, S = 0 sets no bound.
  * out: [Q, heads, 512] f32; lse: [Q, heads] f32 or NULL.
  * W above DSA_MAX_MLA_WIDTH or kv_rows above 2^31 - 1 is refused with DSA_ERR_UNSUPPORTED.
  * ws: device workspace of at least dsa_sparse_mla_decode_workspace(cfg, Q, W) bytes

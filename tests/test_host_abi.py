@@ -185,6 +185,16 @@ def test_refusals_return_codes_without_launching():
     assert L.dsa_sparse_mla_decode(c, 32, 4096, 32, 0.0625, _FAKE, _FAKE, _FAKE, _FAKE, 2,
                                    _NULL, 1 << 20, 131072, _NULL, 0, 64, _FAKE, _NULL, _FAKE,
                                    need, _NULL) == -1
+    # a contiguous latent (no block table) needs a positive stride S: with S = 0 every
+    # sequence would read sequence 0's rows
+    for S in (0, -1):
+        assert L.dsa_sparse_mla_decode(c, 2, 8, 2, 0.0625, _FAKE, _FAKE, _FAKE, _FAKE, 0, _NULL,
+                                       1 << 20, S, _NULL, 0, 64, _FAKE, _NULL, _NULL, 0,
+                                       _NULL) == -2
+    # paged, S = 0 only means no bound on the token ids: accepted up to the workspace check
+    assert L.dsa_sparse_mla_decode(c, 32, 4096, 32, 0.0625, _FAKE, _FAKE, _FAKE, _FAKE, 0,
+                                   _NULL, 1 << 20, 0, _FAKE, 2048, 64, _FAKE, _NULL, _NULL, 0,
+                                   _NULL) == -12
     assert L.dsa_sparse_mla_decode(ctypes.byref(_cfg(kv_lora_rank=576)), 1, 8, 1, 0.0625, _FAKE,
                                    _FAKE, _FAKE, _FAKE, 0, _NULL, 64, 64, _NULL, 0, 64, _FAKE,
                                    _NULL, _NULL, 0, _NULL) == -8
