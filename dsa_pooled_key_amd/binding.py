@@ -39,7 +39,7 @@ EXPORTED = [
     "dsa_compact_index_scores",
     "dsa_topk_workspace", "dsa_topk_pools_workspace", "dsa_topk_pools", "dsa_expand_selection", "dsa_topk_expand",
     "dsa_sparse_mla_decode_workspace",
-    "dsa_sparse_mla_decode", "dsa_absorb_q", "dsa_absorb_o", "dsa_f32_to_bf16_rne",
+    "dsa_sparse_mla_decode", "dsa_sparse_mla_decode_noalloc", "dsa_absorb_q", "dsa_absorb_o", "dsa_f32_to_bf16_rne",
 ]
 
 
@@ -109,6 +109,8 @@ def lib():
             "dsa_sparse_mla_decode_workspace": ([_CFG, _I, _I], _SZ),
             "dsa_sparse_mla_decode": ([_CFG, _I, _I, _I, _F, _P, _P, _P, _P, _I, _P, _I64, _I,
                                        _P, _I, _I, _P, _P, _P, _SZ, _P], _I),
+            "dsa_sparse_mla_decode_noalloc": ([_CFG, _I, _I, _I, _F, _P, _P, _P, _P, _I, _P,
+                                               _I64, _I, _P, _I, _I, _P, _P, _P], _I),
             "dsa_absorb_q": ([_CFG, _P, _SZ, _P, _SZ, _I, _I, _P, _SZ], _I),
             "dsa_absorb_o": ([_CFG, _P, _SZ, _P, _SZ, _I, _I, _P, _SZ], _I),
             "dsa_f32_to_bf16_rne": ([_P, _P, _SZ], None),
@@ -492,13 +494,7 @@ def sparse_mla_workspace(cfg: Config, Q: int, W: int) -> int:
     return int(lib().dsa_sparse_mla_decode_workspace(ctypes.byref(cfg), Q, W))
 
 
-def sparse_mla_decode(cfg: Config, q_abs, token_ids, row_seq, kv, *, B: int, sm_scale: float,
-                      S: int, kv_scales=None, block_table=None, block_size: int = 64,
-                      out=None, lse=None, ws=None):
-    """q_abs [Q,H,512] bf16; token_ids [Q,W] i32; kv [rows,512] bf16 or fp8 (+ kv_scales
-    [rows] f32); contiguous rows b*S + t (S > 0 required), or paged through block_table
-    [B, max_blocks] (S > 0 also bounds the token ids; 0 = no bound).
-    Returns (out [Q,H,512] f32, lse [Q,H] f32)."""
+def _mla_args(cfg: Config, q_abs, token_ids, row_seq, kv, B, kv_scales, block_table, out, lse):
     _dev(q_abs, "q_abs", (torch.bfloat16,))
     Q, H, C = q_abs.shape
     if H != cfg.heads or C != 512:
@@ -529,6 +525,18 @@ def sparse_mla_decode(cfg: Config, q_abs, token_ids, row_seq, kv, *, B: int, sm_
         lse = torch.empty((Q, H), dtype=torch.float32, device=q_abs.device)
     _dev(out, "out", (torch.float32,), (Q, H, 512))
     _dev(lse, "lse", (torch.float32,), (Q, H))
+    return Q, W, rows, code, max_blocks, out, lse
+
+
+def sparse_mla_decode(cfg: Config, q_abs, token_ids, row_seq, kv, *, B: int, sm_scale: float,
+                      S: int, kv_scales=None, block_table=None, block_size: int = 64,
+                      out=None, lse=None, ws=None):
+    """q_abs [Q,H,512] bf16; token_ids [Q,W] i32; kv [rows,512] bf16 or fp8 (+ kv_scales
+    [rows] f32); contiguous rows b*S + t (S > 0 required), or paged through block_table
+    [B, max_blocks] (S > 0 also bounds the token ids; 0 = no bound).
+    Returns (out [Q,H,512] f32, lse [Q,H] f32)."""
+    Q, W, rows, code, max_blocks, out, lse = _mla_args(cfg, q_abs, token_ids, row_seq, kv, B,
+                                                       kv_scales, block_table, out, lse)
     need = sparse_mla_workspace(cfg, Q, W)
     if need and ws is None:
         ws = torch.empty((need,), dtype=torch.uint8, device=q_abs.device)
@@ -538,6 +546,21 @@ def sparse_mla_decode(cfg: Config, q_abs, token_ids, row_seq, kv, *, B: int, sm_
                                        _ptr(kv_scales) if code == DSA_FP8_E4M3 else None, rows,
                                        S, _ptr(block_table), max_blocks, block_size, _ptr(out),
                                        _ptr(lse), _ptr(ws), ws_bytes, _stream(q_abs)))
+    return out, lse
+
+
+def sparse_mla_decode_noalloc(cfg: Config, q_abs, token_ids, row_seq, kv, *, B: int,
+                              sm_scale: float, S: int, kv_scales=None, block_table=None,
+                              block_size: int = 64, out=None, lse=None):
+    """sparse_mla_decode with the split partials in the library's fixed device scratch: pass
+    out and lse to allocate nothing at all. Refuses (DSA_ERR_WORKSPACE) a shape whose
+    partials exceed the scratch."""
+    Q, W, rows, code, max_blocks, out, lse = _mla_args(cfg, q_abs, token_ids, row_seq, kv, B,
+                                                       kv_scales, block_table, out, lse)
+    _check(lib().dsa_sparse_mla_decode_noalloc(
+        ctypes.byref(cfg), Q, W, B, float(sm_scale), _ptr(q_abs), _ptr(token_ids), _ptr(row_seq),
+        _ptr(kv), code, _ptr(kv_scales) if code == DSA_FP8_E4M3 else None, rows, S,
+        _ptr(block_table), max_blocks, block_size, _ptr(out), _ptr(lse), _stream(q_abs)))
     return out, lse
 
 

@@ -457,12 +457,18 @@ size_t dsa_sparse_mla_decode_workspace(const dsa_config *cfg, int Q, int W) {
     return dsa::plan_sparse_mla(Q, W, cfg->heads).ws_bytes;
 }
 
-int dsa_sparse_mla_decode(const dsa_config *cfg, int Q, int W, int B, float sm_scale,
-                          const void *q_abs, const int32_t *token_ids, const int32_t *row_seq,
-                          const void *kv, dsa_dtype kv_dtype, const float *kv_scales,
-                          int64_t kv_rows, int S, const int32_t *block_table, int max_blocks,
-                          int block_size, float *out, float *lse, void *ws, size_t ws_bytes,
-                          hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// dsa_sparse_mla_decode and its no-allocation variant: the same checks and launches; with
+// noalloc the split partials go to the library's fixed device scratch instead of ws.
+int sparse_mla_decode_impl(const dsa_config *cfg, int Q, int W, int B, float sm_scale,
+                           const void *q_abs, const int32_t *token_ids, const int32_t *row_seq,
+                           const void *kv, dsa_dtype kv_dtype, const float *kv_scales,
+                           int64_t kv_rows, int S, const int32_t *block_table, int max_blocks,
+                           int block_size, float *out, float *lse, void *ws, size_t ws_bytes,
+                           bool noalloc, hipStream_t stream) {
     clear_error();
     int rc = check_config(cfg);
     if (rc) return rc;
@@ -491,14 +497,53 @@ int dsa_sparse_mla_decode(const dsa_config *cfg, int Q, int W, int B, float sm_s
     if (!aligned(q_abs, 16) || (kv && !aligned(kv, 16)) || !aligned(out, 16))
         return set_error(DSA_ERR_BAD_SIZE, "sparse_mla_decode: q_abs, kv and out need 16-byte alignment");
     const dsa::MlaPlan plan = dsa::plan_sparse_mla(Q, W, cfg->heads);
-    if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned(ws, 16)))
+    if (noalloc) {
+        if (plan.ws_bytes > dsa::kMlaNoallocScratchBytes)
+            return set_error(DSA_ERR_WORKSPACE,
+                             "sparse_mla_decode_noalloc: Q = %d, W = %d needs %zu bytes of split "
+                             "partials, above the %zu-byte fixed scratch (use dsa_sparse_mla_decode "
+                             "with a workspace)",
+                             Q, W, plan.ws_bytes, dsa::kMlaNoallocScratchBytes);
+        ws = nullptr;
+        if (plan.ws_bytes > 0) {
+            const hipError_t e = dsa::mla_noalloc_scratch(&ws);
+            if (e != hipSuccess) return hip_status(e, "sparse_mla_decode_noalloc scratch lookup");
+        }
+    } else if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned(ws, 16))) {
         return set_error(DSA_ERR_WORKSPACE, "sparse_mla_decode: needs a 16-byte aligned workspace of %zu bytes",
                     plan.ws_bytes);
+    }
     return hip_status(dsa::launch_sparse_mla(plan, Q, W, cfg->heads, B, sm_scale,
                                              static_cast<const uint16_t *>(q_abs), token_ids,
                                              row_seq, kv, fp8, kv_scales, kv_rows, S, block_table,
                                              max_blocks, block_size, out, lse, ws, stream),
                       "sparse_mla_decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_sparse_mla_decode(const dsa_config *cfg, int Q, int W, int B, float sm_scale,
+                          const void *q_abs, const int32_t *token_ids, const int32_t *row_seq,
+                          const void *kv, dsa_dtype kv_dtype, const float *kv_scales,
+                          int64_t kv_rows, int S, const int32_t *block_table, int max_blocks,
+                          int block_size, float *out, float *lse, void *ws, size_t ws_bytes,
+                          hipStream_t stream) {
+    return sparse_mla_decode_impl(cfg, Q, W, B, sm_scale, q_abs, token_ids, row_seq, kv, kv_dtype,
+                                  kv_scales, kv_rows, S, block_table, max_blocks, block_size, out,
+                                  lse, ws, ws_bytes, false, stream);
+}
+
+int dsa_sparse_mla_decode_noalloc(const dsa_config *cfg, int Q, int W, int B, float sm_scale,
+                                  const void *q_abs, const int32_t *token_ids,
+                                  const int32_t *row_seq, const void *kv, dsa_dtype kv_dtype,
+                                  const float *kv_scales, int64_t kv_rows, int S,
+                                  const int32_t *block_table, int max_blocks, int block_size,
+                                  float *out, float *lse, hipStream_t stream) {
+    return sparse_mla_decode_impl(cfg, Q, W, B, sm_scale, q_abs, token_ids, row_seq, kv, kv_dtype,
+                                  kv_scales, kv_rows, S, block_table, max_blocks, block_size, out,
+                                  lse, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

@@ -92,6 +92,10 @@ struct MlaPlan {
     size_t ws_bytes; // partial results for parts > 1
 };
 MlaPlan plan_sparse_mla(int Q, int W, int H);
+// Size of the fixed device scratch behind dsa_sparse_mla_decode_noalloc, and its address on
+// the current device (looked up once per device, then cached).
+constexpr size_t kMlaNoallocScratchBytes = DSA_MLA_NOALLOC_SCRATCH_BYTES;
+hipError_t mla_noalloc_scratch(void **ptr);
 hipError_t launch_sparse_mla(const MlaPlan &plan, int Q, int W, int H, int B, float sm_scale,
                              const uint16_t *q_abs, const int32_t *token_ids,
                              const int32_t *row_seq, const void *kv, bool kv_fp8,

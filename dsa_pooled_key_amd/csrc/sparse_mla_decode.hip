@@ -23,10 +23,39 @@
 // unnormalised O) to the workspace and mla_combine merges them.
 //
 // Bytes per selected token: 1024 (bf16) or 516 (fp8 + scale) of latent, 4 of token id.
+#include <mutex>
+
 #include "dsa_device.hpp"
 #include "dsa_launch.hpp"
 
 namespace dsa {
+
+// Fixed device scratch for dsa_sparse_mla_decode_noalloc: the split partials live here instead
+// of in a caller's workspace. Each GPU the library runs on holds its own copy for the life of
+// the process. In host code this name is only a stand-in for the symbol; kernels get the device
+// address that mla_noalloc_scratch() looks up.
+__device__ __attribute__((aligned(256))) uint8_t scratch[kMlaNoallocScratchBytes];
+
+hipError_t mla_noalloc_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
 namespace {
 
 constexpr int kC = 512;

@@ -300,6 +300,24 @@ int dsa_sparse_mla_decode(const dsa_config *cfg, int Q, int W, int B, float sm_s
                           int block_size, float *out, float *lse, void *ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): dsa_sparse_mla_decode without the workspace
+ * argument. The split partials go to a fixed 16 MiB device array inside the library
+ * (DSA_MLA_NOALLOC_SCRATCH_BYTES), one copy per GPU, held until the process ends and looked
+ * up on the first call on each device; nothing is allocated, and the result is bit-identical
+ * to dsa_sparse_mla_decode's. Arguments, layouts and refusals are those of
+ * dsa_sparse_mla_decode; a call whose workspace query exceeds the scratch size is refused
+ * with DSA_ERR_WORKSPACE before anything is launched. Every call on one GPU shares that GPU's
+ * scratch, which keeps the last call's partials: calls that overlap on one GPU (different
+ * streams, or threads) race and must be ordered by the caller. */
+#define DSA_MLA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int dsa_sparse_mla_decode_noalloc(const dsa_config *cfg, int Q, int W, int B, float sm_scale,
+                                  const void *q_abs, const int32_t *token_ids,
+                                  const int32_t *row_seq, const void *kv, dsa_dtype kv_dtype,
+                                  const float *kv_scales, int64_t kv_rows, int S,
+                                  const int32_t *block_table, int max_blocks, int block_size,
+                                  float *out, float *lse, hipStream_t stream);
+
 /* ------------------------------------------------------------------ dense masked cross-check */
 /* mod.rs, Glm5NextDsaKernels::{topk_to_mask, mla_masked_attn} and MASKED_ATTN_MAX_KEYS: the
  * selection as a token mask, and a dense attention over every masked token that stages the
