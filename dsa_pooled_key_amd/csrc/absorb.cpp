@@ -1,65 +1,73 @@
-// absorb.cpp -- host-side load-time weight transforms (build.rs, absorb_q, absorb_o, up_bf16).
+// absorb.cpp -- host-side load-time weight transforms (build.rs, "The transforms" 1 and 3,
+// absorb_q, absorb_o) and the bf16 upload rounding (up_bf16).
 //
-// Compiled with -ffp-contract=off: each output element is accumulated in f32 as
-// acc = acc + (a * b), r ascending, inside one thread, so the result is bit-identical for
-// any thread count (build.rs, absorb_q_rows: the absorb_q_bit_exact property).
-#include <cerrno>
-#include <cstdarg>
-#include <cstdio>
+// Both transforms are products over the no-position (or value) width r of one head:
+//   q_absorb[h*kvl + c][k]   = sum_{r < nope} kv_b[h*(nope+vd) + r][c] * q_b[h*nope + r][k]
+//   o_absorb[i][h*kvl + c]   = sum_{r < vd}   o_proj[i][h*vd + r] * kv_b[h*(nope+vd) + nope + r][c]
+// The pages require the result to be bit-identical for any number of threads, which fixes the
+// arithmetic of each element: a binary32 sum from 0 over r ascending, each product rounded
+// before it is added (this file is compiled with -ffp-contract=off). Everything else is free:
+// here the work is cut into tiles (one head times a block of output columns), each tile owned
+// by one thread and swept r-outermost, so a tile's accumulators stay in cache while the
+// weight rows stream past once.
+#include <algorithm>
+#include <cctype>
 #include <cstdlib>
 #include <cstring>
+#include <string>
 #include <thread>
 #include <vector>
 
 #include "dsa.h"
 #include "dsa_host.hpp"
 
-namespace dsa_host {
+namespace {
 
-// Worker threads: an explicit positive count, else the DSA_ABSORB_THREADS environment variable
-// when it parses as a positive integer, else the hardware concurrency; clamped to 1..rows
-// (build.rs, absorb_threads).
-size_t absorb_threads(int requested, size_t rows) {
-    size_t want = 0;
-    if (requested > 0) {
-        want = (size_t)requested;
-    } else {
-        const char *env = std::getenv("DSA_ABSORB_THREADS");
-        if (env) {
-            while (*env == ' ' || *env == '\t' || *env == '\n') ++env;
-            char *end = nullptr;
-            errno = 0;
-            const long long v = std::strtoll(env, &end, 10);
-            while (end && (*end == ' ' || *end == '\t' || *end == '\n')) ++end;
-            if (errno == 0 && end && *end == 0 && end != env && v > 0) want = (size_t)v;
-        }
-        if (want == 0) {
-            const unsigned hc = std::thread::hardware_concurrency();
-            want = hc > 0 ? hc : 1;
-        }
-    }
-    if (rows == 0) rows = 1;
-    if (want < 1) want = 1;
-    if (want > rows) want = rows;
-    return want;
+constexpr size_t kColBlock = 64;   // output columns per tile (absorb_q: k; absorb_o: rows i)
+
+// A positive integer from the environment (surrounding blanks allowed), else 0.
+long long env_positive(const char *name) {
+    const char *raw = std::getenv(name);
+    if (raw == nullptr) return 0;
+    std::string t(raw);
+    const auto blank = [](unsigned char ch) { return std::isspace(ch) != 0; };
+    while (!t.empty() && blank(t.back())) t.pop_back();
+    size_t i = 0;
+    while (i < t.size() && blank(t[i])) ++i;
+    t.erase(0, i);
+    if (t.empty() || t.size() > 18) return 0;
+    for (unsigned char ch : t)
+        if (ch < '0' || ch > '9') return 0;
+    return std::atoll(t.c_str());
 }
 
+// Worker count (build.rs, absorb_threads): the explicit argument when positive, else
+// DSA_ABSORB_THREADS when it holds a positive integer, else the hardware concurrency; never
+// more workers than work items, never fewer than one. It changes speed only, not results.
+size_t worker_count(int requested, size_t items) {
+    long long n = requested > 0 ? requested : env_positive("DSA_ABSORB_THREADS");
+    if (n <= 0) n = (long long)std::thread::hardware_concurrency();
+    const long long cap = (long long)std::max<size_t>(items, 1);
+    return (size_t)std::clamp<long long>(n, 1, cap);
+}
+
+// Run body(item) for item in [0, items) on `workers` threads, items dealt round-robin.
 template <class F>
-void run_spans(size_t rows, size_t threads, F &&body) {
-    if (threads <= 1) {
-        body(0, rows);
+void parallel_items(size_t items, size_t workers, F &&body) {
+    if (workers <= 1) {
+        for (size_t it = 0; it < items; ++it) body(it);
         return;
     }
-    const size_t per = (rows + threads - 1) / threads;
     std::vector<std::thread> pool;
-    for (size_t r0 = 0; r0 < rows; r0 += per) {
-        const size_t r1 = r0 + per < rows ? r0 + per : rows;
-        pool.emplace_back([&body, r0, r1] { body(r0, r1); });
-    }
+    pool.reserve(workers);
+    for (size_t w = 0; w < workers; ++w)
+        pool.emplace_back([&body, w, workers, items] {
+            for (size_t it = w; it < items; it += workers) body(it);
+        });
     for (auto &t : pool) t.join();
 }
 
-}  // namespace dsa_host
+}  // namespace
 
 extern "C" {
 
@@ -71,8 +79,9 @@ int dsa_absorb_q(const dsa_config *cfg, const float *q_b, size_t q_b_len, const 
     if (full_heads < 0 || cfg->qk_nope_head_dim < 0 || cfg->qk_rope_head_dim < 0 ||
         cfg->v_head_dim < 0 || cfg->kv_lora_rank < 0 || cfg->q_lora_rank < 0)
         return set_error(DSA_ERR_BAD_SIZE, "absorb_q: negative dimension");
-    const size_t nope = cfg->qk_nope_head_dim, vd = cfg->v_head_dim, kvl = cfg->kv_lora_rank,
-                 ql = cfg->q_lora_rank, rope = cfg->qk_rope_head_dim, heads = full_heads;
+    const size_t heads = (size_t)full_heads, nope = (size_t)cfg->qk_nope_head_dim,
+                 rope = (size_t)cfg->qk_rope_head_dim, vd = (size_t)cfg->v_head_dim,
+                 kvl = (size_t)cfg->kv_lora_rank, ql = (size_t)cfg->q_lora_rank;
     if (q_b_len != heads * (nope + rope) * ql)
         return set_error(DSA_ERR_ELEM_COUNT, "absorb_q: q_b has %zu elements, the config needs %zu",
                          q_b_len, heads * (nope + rope) * ql);
@@ -82,22 +91,26 @@ int dsa_absorb_q(const dsa_config *cfg, const float *q_b, size_t q_b_len, const 
     if (rope != 0)
         return set_error(DSA_ERR_ROPE_UNSUPPORTED,
                          "absorb_q: only NoPE can be absorbed (qk_rope_head_dim is %zu)", rope);
-    const size_t rows = heads * kvl;
-    if (out_len != rows * ql)
+    if (out_len != heads * kvl * ql)
         return set_error(DSA_ERR_ELEM_COUNT, "absorb_q: out has %zu elements, needs %zu", out_len,
-                         rows * ql);
-    if (rows * ql == 0) return DSA_OK;
+                         heads * kvl * ql);
+    if (out_len == 0) return DSA_OK;
     if (!q_b || !kv_b || !out) return set_error(DSA_ERR_NULL_ARG, "absorb_q: a buffer is NULL");
-    const size_t nt = dsa_host::absorb_threads(threads, rows);
-    dsa_host::run_spans(rows, nt, [&](size_t r0, size_t r1) {
-        for (size_t row = r0; row < r1; ++row) {
-            const size_t h = row / kvl, c = row % kvl;
-            float *acc = out + row * ql;
-            for (size_t k = 0; k < ql; ++k) acc[k] = 0.0f;
-            for (size_t r = 0; r < nope; ++r) {
-                const float wv = kv_b[(h * (nope + vd) + r) * kvl + c];
-                const float *qrow = q_b + (h * nope + r) * ql;
-                for (size_t k = 0; k < ql; ++k) acc[k] = acc[k] + qrow[k] * wv;
+    // Tile (h, kb): output rows h*kvl .. h*kvl + kvl - 1, columns kb*kColBlock .. + kColBlock.
+    const size_t kblocks = (ql + kColBlock - 1) / kColBlock;
+    const size_t tiles = heads * kblocks;
+    parallel_items(tiles, worker_count(threads, tiles), [&](size_t tile) {
+        const size_t h = tile / kblocks, k0 = (tile % kblocks) * kColBlock;
+        const size_t kn = std::min(kColBlock, ql - k0);
+        float *const t0 = out + h * kvl * ql + k0;
+        for (size_t c = 0; c < kvl; ++c) std::memset(t0 + c * ql, 0, kn * sizeof(float));
+        for (size_t r = 0; r < nope; ++r) {
+            const float *const weights = kv_b + (h * (nope + vd) + r) * kvl;   // kv_b row, over c
+            const float *const qv = q_b + (h * nope + r) * ql + k0;           // q_b row, over k
+            for (size_t c = 0; c < kvl; ++c) {
+                const float wc = weights[c];
+                float *const o = t0 + c * ql;
+                for (size_t j = 0; j < kn; ++j) o[j] = o[j] + wc * qv[j];
             }
         }
     });
@@ -117,8 +130,9 @@ int dsa_absorb_o(const dsa_config *cfg, const float *o_local, size_t o_len,
         return set_error(DSA_ERR_ROPE_UNSUPPORTED,
                          "absorb_o: only NoPE can be absorbed (qk_rope_head_dim is %d)",
                          cfg->qk_rope_head_dim);
-    const size_t nope = cfg->qk_nope_head_dim, vd = cfg->v_head_dim, kvl = cfg->kv_lora_rank,
-                 hidden = cfg->hidden, heads = local_heads;
+    const size_t heads = (size_t)local_heads, nope = (size_t)cfg->qk_nope_head_dim,
+                 vd = (size_t)cfg->v_head_dim, kvl = (size_t)cfg->kv_lora_rank,
+                 hidden = (size_t)cfg->hidden;
     const size_t in_w = heads * vd, out_w = heads * kvl;
     if (o_len != hidden * in_w)
         return set_error(DSA_ERR_ELEM_COUNT, "absorb_o: o_proj has %zu elements, expected %zu",
@@ -129,22 +143,22 @@ int dsa_absorb_o(const dsa_config *cfg, const float *o_local, size_t o_len,
     if (out_len != hidden * out_w)
         return set_error(DSA_ERR_ELEM_COUNT, "absorb_o: out has %zu elements, needs %zu", out_len,
                          hidden * out_w);
-    if (hidden * out_w == 0) return DSA_OK;
-    if (!o_local || !kv_b_local || !out) return set_error(DSA_ERR_NULL_ARG, "absorb_o: a buffer is NULL");
-    const size_t nt = dsa_host::absorb_threads(threads, hidden);
-    dsa_host::run_spans(hidden, nt, [&](size_t i0, size_t i1) {
-        for (size_t i = i0; i < i1; ++i) {
-            float *dst_row = out + i * out_w;
-            const float *src_row = o_local + i * in_w;
-            for (size_t k = 0; k < out_w; ++k) dst_row[k] = 0.0f;
-            for (size_t h = 0; h < heads; ++h) {
-                float *dst = dst_row + h * kvl;
-                const size_t v_base = h * (nope + vd) + nope;
-                for (size_t r = 0; r < vd; ++r) {
-                    const float wv = src_row[h * vd + r];
-                    const float *src = kv_b_local + (v_base + r) * kvl;
-                    for (size_t c = 0; c < kvl; ++c) dst[c] = dst[c] + wv * src[c];
-                }
+    if (out_len == 0) return DSA_OK;
+    if (!o_local || !kv_b_local || !out)
+        return set_error(DSA_ERR_NULL_ARG, "absorb_o: a buffer is NULL");
+    // Tile (h, ib): output rows ib*kColBlock .. + kColBlock, columns h*kvl .. h*kvl + kvl - 1.
+    const size_t iblocks = (hidden + kColBlock - 1) / kColBlock;
+    const size_t tiles = heads * iblocks;
+    parallel_items(tiles, worker_count(threads, tiles), [&](size_t tile) {
+        const size_t h = tile / iblocks, i0 = (tile % iblocks) * kColBlock;
+        const size_t in_ = std::min(kColBlock, hidden - i0);
+        for (size_t i = i0; i < i0 + in_; ++i) std::memset(out + i * out_w + h * kvl, 0, kvl * sizeof(float));
+        for (size_t r = 0; r < vd; ++r) {
+            const float *const vrow = kv_b_local + (h * (nope + vd) + nope + r) * kvl;  // over c
+            for (size_t i = i0; i < i0 + in_; ++i) {
+                const float oi = o_local[i * in_w + h * vd + r];
+                float *const o = out + i * out_w + h * kvl;
+                for (size_t c = 0; c < kvl; ++c) o[c] = o[c] + oi * vrow[c];
             }
         }
     });

@@ -609,11 +609,24 @@ static void put_msg(char *msg, int msg_len, const char *text) {
     }
 }
 
-/* build.rs, absorb_q and absorb_q_rows: out[h*kvl + c][k] =
- * sum over r < nope of kv_b[h*(nope+vd) + r][c] * q_b[h*nope + r][k], in f32 with r ascending,
- * accumulating acc[k] += q * w (separate multiply and add). Refuses wrong element counts
- * (q_b must be [heads*(nope+rope), ql], kv_b [heads*(nope+vd), kvl]) and a nonzero rope
- * width. Returns 0, or 1 (q_b count), 2 (kv_b count), 3 (rope). out is [heads*kvl, ql]. */
+/* One element of either absorption (build.rs, "The transforms" 1 and 3): the binary32 sum,
+ * started at 0 and taken over r = 0, 1, ..., n-1 in that order, of the rounded products
+ * a[r*sa] * b[r*sb]. The bit-exact absorption fixes exactly this arithmetic (the file is
+ * compiled with -ffp-contract=off, so no product is fused into its addition). */
+static float dot_f32_ascending(const float *a, long sa, const float *b, long sb, long n) {
+    float sum = 0.0f;
+    for (long r = 0; r < n; ++r) {
+        float term = a[r * sa] * b[r * sb];
+        sum = sum + term;
+    }
+    return sum;
+}
+
+/* build.rs, absorb_q: q_absorb[h*kvl + c][k] = sum over r < nope of
+ * kv_b[h*(nope+vd) + r][c] * q_b[h*nope + r][k], each element by dot_f32_ascending. Refuses
+ * wrong element counts (q_b must be [heads*(nope+rope), ql], kv_b [heads*(nope+vd), kvl]) and
+ * a nonzero rope width. Returns 0, or 1 (q_b count), 2 (kv_b count), 3 (rope). out is
+ * [heads*kvl, ql]. */
 int orc_absorb_q(int heads, int nope, int rope, int vd, int kvl, int ql, const float *q_b,
                  long q_b_len, const float *kv_b, long kv_b_len, float *out, char *msg,
                  int msg_len) {
@@ -629,28 +642,21 @@ int orc_absorb_q(int heads, int nope, int rope, int vd, int kvl, int ql, const f
         put_msg(msg, msg_len, "absorption is defined for NoPE only (rope width must be 0)");
         return 3;
     }
-    long rows = (long)heads * kvl;
-    for (long row = 0; row < rows; ++row) {
-        long h = row / kvl, c = row % kvl;
-        float *acc = out + row * ql;
-        for (long k = 0; k < ql; ++k) acc[k] = 0.0f;
-        for (long r = 0; r < nope; ++r) {
-            float wv = kv_b[(h * (nope + vd) + r) * kvl + c];
-            const float *q_row = q_b + (h * nope + r) * ql;
-            for (long k = 0; k < ql; ++k) {
-                float prod = q_row[k] * wv;
-                acc[k] = acc[k] + prod;
-            }
-        }
-    }
+    for (long h = 0; h < heads; ++h)
+        for (long c = 0; c < kvl; ++c)
+            for (long k = 0; k < ql; ++k)
+                out[(h * kvl + c) * ql + k] =
+                    dot_f32_ascending(kv_b + (h * (nope + vd)) * kvl + c, kvl,   /* over r: kv_b[.][c] */
+                                      q_b + (h * nope) * ql + k, ql,             /* over r: q_b[.][k] */
+                                      nope);
     return 0;
 }
 
-/* build.rs, absorb_o: o_absorb[i][h*kvl + c] =
- * sum over r < vd of o_proj[i][h*vd + r] * kv_b[h*(nope+vd) + nope + r][c], f32, r ascending,
- * dst += w * k (separate multiply and add). Refuses a nonzero rope width and wrong counts
- * (o_local [hidden, heads*vd], kv_b_local [heads*(nope+vd), kvl]). Returns 0, or 3 (rope),
- * 1 (o_proj count), 2 (kv_b count), checked in that order. out is [hidden, heads*kvl]. */
+/* build.rs, absorb_o: o_absorb[i][h*kvl + c] = sum over r < vd of
+ * o_proj[i][h*vd + r] * kv_b[h*(nope+vd) + nope + r][c], each element by dot_f32_ascending.
+ * Refuses a nonzero rope width and wrong counts (o_local [hidden, heads*vd], kv_b_local
+ * [heads*(nope+vd), kvl]). Returns 0, or 3 (rope), 1 (o_proj count), 2 (kv_b count), checked
+ * in that order. out is [hidden, heads*kvl]. */
 int orc_absorb_o(int heads, int nope, int rope, int vd, int kvl, int hidden, const float *o_local,
                  long o_len, const float *kv_b_local, long kv_len, float *out, char *msg,
                  int msg_len) {
@@ -667,20 +673,12 @@ int orc_absorb_o(int heads, int nope, int rope, int vd, int kvl, int hidden, con
         put_msg(msg, msg_len, "kv_b element count does not match heads*(nope+v)*kv_lora_rank");
         return 2;
     }
-    for (long i = 0; i < (long)hidden * out_w; ++i) out[i] = 0.0f;
-    for (long i = 0; i < hidden; ++i) {
-        for (long h = 0; h < heads; ++h) {
-            float *dst = out + i * out_w + h * kvl;
-            long v_base = h * (nope + vd) + nope;
-            for (long r = 0; r < vd; ++r) {
-                float wv = o_local[i * in_w + h * vd + r];
-                const float *src = kv_b_local + (v_base + r) * kvl;
-                for (long c = 0; c < kvl; ++c) {
-                    float prod = wv * src[c];
-                    dst[c] = dst[c] + prod;
-                }
-            }
-        }
-    }
+    for (long i = 0; i < hidden; ++i)
+        for (long h = 0; h < heads; ++h)
+            for (long c = 0; c < kvl; ++c)
+                out[i * out_w + h * kvl + c] =
+                    dot_f32_ascending(o_local + i * in_w + h * vd, 1,                   /* o_proj[i][h*vd + r] */
+                                      kv_b_local + (h * (nope + vd) + nope) * kvl + c, kvl,  /* kv_b[.][c] */
+                                      vd);
     return 0;
 }

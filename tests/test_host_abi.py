@@ -98,6 +98,20 @@ def test_absorb_o_is_thread_count_invariant_and_equals_oracle():
         assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), t
 
 
+@pytest.mark.parametrize("threads", [1, 3, 0])
+def test_absorb_several_column_blocks_equal_oracle(threads):
+    """Widths that cut the product's tiles raggedly (q_lora_rank 200 and hidden 150 over
+    64-column blocks, two heads): bit-identical to the oracle's per-element sums at one,
+    three and all threads."""
+    cfg, q_b, kv_b, o = _absorb_case(7, heads=2, nope=16, vd=12, kvl=512, ql=200, hidden=150)
+    rq = oracle.absorb_q(q_b, kv_b, heads=2, nope=16, rope=0, vd=12, kvl=512, ql=200)
+    ro = oracle.absorb_o(o, kv_b, heads=2, nope=16, rope=0, vd=12, kvl=512, hidden=150)
+    gq = dsa.absorb_q(cfg, q_b, kv_b, full_heads=2, threads=threads)
+    go = dsa.absorb_o(cfg, o, kv_b, local_heads=2, threads=threads)
+    assert np.array_equal(gq.view(np.uint32), rq.view(np.uint32))
+    assert np.array_equal(go.view(np.uint32), ro.view(np.uint32))
+
+
 def test_absorb_refusals():
     cfg, q_b, kv_b, o = _absorb_case(3)
     with pytest.raises(dsa.DsaError) as e:
