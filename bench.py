@@ -223,17 +223,23 @@ def extra_lines(args):
     extra = {}
     if not args.no_masked:
         extra["masked_check"] = masked_check_line(args)
-    if not args.no_x128:
-        r = run_chain("decode_b8_128k", args.extra_steps, args.warmup, args.seed)
+    def decode_line(name, what):
+        r = run_chain(name, args.extra_steps, args.warmup, args.seed)
         wl = r["di"].wl
         gbs = r["alg"]["step"] / (r["ms"] * 1e-3) / 1e9
-        extra["x128"] = {
-            "workload": f"{wl.name}: {wl.Q} decode queries, every context {wl.S}, kpool {wl.kpool}, "
-                        f"topk {wl.topk}, bf16 keys and latent, contiguous",
-            "queries_per_s": round(wl.Q / (r["ms"] * 1e-3), 1), "ms_per_step": round(r["ms"], 5),
-            "steps": r["steps"], "replicas": r["reps"],
-            "algorithmic_bytes": r["alg"]["step"], "achieved_GBs": round(gbs, 1),
-            "frac_of_peak_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+        return {"workload": f"{wl.name}: {wl.Q} decode queries, {what}, kpool {wl.kpool}, "
+                            f"topk {wl.topk}, bf16 keys and latent, "
+                            f"{'paged 64-token blocks' if wl.paged else 'contiguous'}",
+                "queries_per_s": round(wl.Q / (r["ms"] * 1e-3), 1), "ms_per_step": round(r["ms"], 5),
+                "steps": r["steps"], "replicas": r["reps"],
+                "algorithmic_bytes": r["alg"]["step"], "achieved_GBs": round(gbs, 1),
+                "frac_of_peak_hbm": round(gbs / PEAK_HBM_GBS, 4)}
+
+    if not args.no_x128:
+        extra["x128"] = decode_line("decode_b8_128k", "every context 131072")
+    if not args.no_decode_lines:
+        extra["decode_b8_32k"] = decode_line("decode_b8_32k", "contexts uniform in [16384, 32768]")
+        extra["decode_b4_256k"] = decode_line("decode_b4_256k", "every context 262144")
     if not args.no_prefill:
         r = run_chain("prefill_2048_64k", args.extra_steps, args.warmup, args.seed)
         wl = r["di"].wl
@@ -247,6 +253,10 @@ def extra_lines(args):
             "flop": flop, "candidate_pools": r["n_cand"], "tokens_attended": r["n_tokens"],
             "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": PEAK_BF16_TFS,
                          "unit": "TFLOP/s", "frac": round(tfs / PEAK_BF16_TFS, 4)}}
+        if not args.no_cpu_baseline:
+            log("timing the CPU oracle on a prefill subsample")
+            extra["prefill"]["cpu_baseline"] = run_cpu_baseline_rows(r["di"], args.prefill_cpu_rows,
+                                                                     args.seed)
     return extra
 
 def run_gpu(args):
@@ -451,6 +461,67 @@ def run_cpu_baseline(di, sample_every: int, min_seconds: float = 10.0, max_passe
                       f"whole decode chain, {passes} passes, {dt:.1f} s wall"}
 
 
+def run_cpu_baseline_rows(di, n_rows: int, seed: int, min_seconds: float = 10.0, max_passes: int = 4):
+    """The oracle's whole chain on a seeded random subsample of n_rows query rows (prefill:
+    rows of one sequence), repeated until min_seconds have passed; rows/s."""
+    import oracle
+
+    wl = di.wl
+    rng = np.random.default_rng(seed + 4242)
+    rows = np.sort(rng.choice(wl.Q, size=min(n_rows, wl.Q), replace=False))
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        ids, nv = oracle.compact_pools(di.pool_valid)
+        rs, rc = oracle.index_scores(di.q[rows], di.w[rows], di.row_seq[rows], di.row_pos[rows],
+                                     di.keys, ids, nv, kpool=wl.kpool, first_key=wl.first_key,
+                                     scale=di.scale, key_scales=di.key_scales)
+        sel = oracle.topk_pools(rs, rc, wl.kw)
+        tok = oracle.expand_selection(sel, di.row_seq[rows], di.row_pos[rows], di.valid,
+                                      kpool=wl.kpool, index_topk=wl.topk,
+                                      always_select_tail=wl.tail, first_key=wl.first_key)
+        oracle.sparse_mla(di.q_abs[rows], tok, di.row_seq[rows], di.kv, sm_scale=di.sm_scale,
+                          S=wl.S, kv_scales=di.kv_scales, block_table=di.block_table)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or passes >= max_passes:
+            break
+    return {"value": round(passes * len(rows) / dt, 2), "unit": "rows/s",
+            "cores": oracle.num_threads(), "host_cpu_count": os.cpu_count(), "kind": "oracle",
+            "sample": f"{len(rows)} of the {wl.Q} rows (seeded random subsample), whole chain, "
+                      f"{passes} passes, {dt:.1f} s wall"}
+
+
+def stream_read_line(replays: int = 10):
+    """The achievable HBM read rate on this GPU: the library's streaming read of a 4 GiB
+    buffer (16 times the Infinity Cache), HIP events around repeated launches."""
+    import torch
+
+    from dsa_pooled_key_amd import binding as dsa
+
+    nbytes = 4 << 30
+    buf = torch.ones((nbytes // 4,), dtype=torch.int32, device="cuda:0")
+    sink = torch.zeros((1,), dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            dsa.stream_read(buf, sink)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(replays):
+            dsa.stream_read(buf, sink)
+        b.record(stream)
+        b.synchronize()
+    ms = a.elapsed_time(b) / replays
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    log(f"streaming read: {gbs:.0f} GB/s over {nbytes >> 30} GiB")
+    return {"GBs": round(gbs, 1), "bytes": nbytes, "launch_us": round(ms * 1e3, 1),
+            "frac_of_nominal_peak": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 # ---------------------------------------------------------------- main
 
 def run_eager(args):
@@ -513,6 +584,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-x128", action="store_true", help="skip the X128 decode line")
     ap.add_argument("--no-prefill", action="store_true", help="skip the C4 prefill line")
+    ap.add_argument("--no-decode-lines", action="store_true",
+                    help="skip the decode_b8_32k and decode_b4_256k lines")
+    ap.add_argument("--prefill-cpu-rows", type=int, default=128,
+                    help="rows of the prefill workload in the oracle's timed subsample")
     ap.add_argument("--no-masked", action="store_true",
                     help="skip the dense masked-attention cross-check line")
     ap.add_argument("--extra-steps", type=int, default=60,
@@ -533,6 +608,7 @@ def main():
         return run_eager(args)
 
     res = run_gpu(args)
+    stream = stream_read_line()
     di, alg, ms = res["di"], res["alg"], res["ms_step"]
     wl = di.wl
     value = wl.Q / (ms * 1e-3)
@@ -585,6 +661,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "frac_of_measured_stream_read": round(achieved / stream["GBs"], 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": alg[dom],
             "launch_us": round(dom_us, 3),
@@ -593,7 +670,9 @@ def main():
             "algorithmic_bytes": alg["step"],
             "achieved_GBs": round(step_gbs, 1),
             "frac_of_peak_hbm": round(step_gbs / PEAK_HBM_GBS, 4),
+            "frac_of_measured_stream_read": round(step_gbs / stream["GBs"], 4),
         },
+        "hbm_stream_read": stream,
         "stage_us": {k: round(v, 3) for k, v in res["stage_us"].items()},
         "kpool_compress": {
             "tokens_per_s": round(kp["tokens"] / (kp["us"] * 1e-6), 1),

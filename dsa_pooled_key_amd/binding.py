@@ -39,7 +39,7 @@ EXPORTED = [
     "dsa_compact_index_scores",
     "dsa_topk_workspace", "dsa_topk_pools_workspace", "dsa_topk_pools", "dsa_expand_selection", "dsa_topk_expand",
     "dsa_sparse_mla_decode_workspace",
-    "dsa_sparse_mla_decode", "dsa_sparse_mla_decode_noalloc", "dsa_absorb_q", "dsa_absorb_o", "dsa_f32_to_bf16_rne",
+    "dsa_sparse_mla_decode", "dsa_sparse_mla_decode_noalloc", "dsa_stream_read", "dsa_absorb_q", "dsa_absorb_o", "dsa_f32_to_bf16_rne",
 ]
 
 
@@ -111,6 +111,7 @@ def lib():
                                        _P, _I, _I, _P, _P, _P, _SZ, _P], _I),
             "dsa_sparse_mla_decode_noalloc": ([_CFG, _I, _I, _I, _F, _P, _P, _P, _P, _I, _P,
                                                _I64, _I, _P, _I, _I, _P, _P, _P], _I),
+            "dsa_stream_read": ([_P, _SZ, _P, _P], _I),
             "dsa_absorb_q": ([_CFG, _P, _SZ, _P, _SZ, _I, _I, _P, _SZ], _I),
             "dsa_absorb_o": ([_CFG, _P, _SZ, _P, _SZ, _I, _I, _P, _SZ], _I),
             "dsa_f32_to_bf16_rne": ([_P, _P, _SZ], None),
@@ -642,3 +643,15 @@ def f32_to_bf16_rne(x) -> np.ndarray:
     lib().dsa_f32_to_bf16_rne(x.ctypes.data_as(ctypes.c_void_p),
                               out.ctypes.data_as(ctypes.c_void_p), x.size)
     return out
+
+
+def stream_read(buf, sink=None):
+    """Measurement only: read every byte of the device tensor buf once (16-byte aligned, a
+    multiple of 16 bytes); the XOR of its 32-bit words is folded into sink (uint32 [1])."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.zeros((1,), dtype=torch.int32, device=buf.device)
+    _check(lib().dsa_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(buf)))
+    return sink

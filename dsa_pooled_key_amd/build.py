@@ -22,7 +22,7 @@ ARCH = "gfx950"
 
 KERNELS = ["kpool_compress.hip", "cache_update.hip", "compact_pools.hip", "index_scores.hip",
            "topk_pools.hip",
-           "expand_selection.hip", "sparse_mla_decode.hip", "masked_attn.hip"]
+           "expand_selection.hip", "sparse_mla_decode.hip", "masked_attn.hip", "stream_read.hip"]
 HOST = ["dsa_api.cpp", "absorb.cpp"]
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]

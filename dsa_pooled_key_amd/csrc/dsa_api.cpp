@@ -546,4 +546,13 @@ int dsa_sparse_mla_decode_noalloc(const dsa_config *cfg, int Q, int W, int B, fl
                                   lse, nullptr, 0, true, stream);
 }
 
+int dsa_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream) {
+    clear_error();
+    if (bytes == 0) return DSA_OK;
+    if (!buf || !sink) return set_error(DSA_ERR_NULL_ARG, "stream_read: a buffer is NULL");
+    if (bytes % 16 != 0 || !aligned(buf, 16) || !aligned(sink, 4))
+        return set_error(DSA_ERR_BAD_SIZE, "stream_read: needs a 16-byte aligned buffer of a multiple of 16 bytes");
+    return hip_status(dsa::launch_stream_read(buf, bytes, sink, 2048, stream), "stream_read launch");
+}
+
 }  // extern "C"

@@ -103,4 +103,8 @@ hipError_t launch_sparse_mla(const MlaPlan &plan, int Q, int W, int H, int B, fl
                              const int32_t *block_table, int max_blocks, int block_size,
                              float *out, float *lse, void *ws, hipStream_t stream);
 
+// Measurement only (stream_read.hip): every 16-byte word of buf read once; sink gets the XOR.
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks,
+                              hipStream_t stream);
+
 }  // namespace dsa

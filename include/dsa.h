@@ -366,6 +366,13 @@ int dsa_absorb_o(const dsa_config *cfg, const float *o_local, size_t o_len,
 /* build.rs, up_bf16: host f32 -> bf16 by round to nearest, ties to even (NaN stays NaN). */
 void dsa_f32_to_bf16_rne(const float *src, uint16_t *dst, size_t n);
 
+/* ------------------------------------------------------------------ measurement only */
+/* Not a step of the method: reads every byte of buf (device memory, 16-byte aligned, bytes a
+ * multiple of 16) once with plain streaming 16-byte loads and XORs the words into *sink (device,
+ * not cleared). The rate it reaches is the achievable HBM read bandwidth that the decode
+ * kernels' bandwidth is reported against, beside the nominal peak. */
+int dsa_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
