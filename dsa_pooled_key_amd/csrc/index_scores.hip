@@ -22,6 +22,11 @@
 //
 // Bytes per candidate pool: D*2 (bf16 key) or D + 4 (fp8 key and scale), plus 4 (id); the
 // score row costs 5 bytes per pool slot.
+#include <algorithm>
+#include <climits>
+#include <cstdint>
+#include <mutex>
+
 #include "dsa_device.hpp"
 #include "dsa_launch.hpp"
 #include "dsa_score_range.hpp"
@@ -187,17 +192,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     fill_tail();
 }
 
-// The compaction and the scoring in one launch: each block scores one (row, chunk) range of
-// pool slots (score_range). With up to kThreads rows, the blocks are renumbered so that the
-// ranges holding candidates come first, row after row, and the ranges past a row's limit
-// after them: block L takes the L-th range of that order. Consecutive blocks are dispatched to
-// different CUs, so a long row's ranges spread over the chip instead of piling onto the CUs
-// that the plain (row, chunk) grid would give them. The order costs one block scan over the
-// rows' positions, read in the same round trip as the row's own geometry.
-template <int D, bool FP8, int TPW>
+// The compaction and the scoring in one launch: each (row, chunk) range of pool slots is scored
+// by score_range. With up to kThreads rows, the ranges are ordered so that those holding
+// candidates come first, row after row, and the ranges past a row's limit after them; the
+// order costs one block scan over the rows' positions. Block j takes range j of that order
+// (consecutive blocks land on different CUs, so a long row's ranges spread over the chip).
+// When the ranges outnumber the blocks resident at once (WALK), the grid holds only that many
+// blocks and each walks its ranges: with fewer ranges holding candidates (A) than blocks, block
+// j < A takes the j-th such range and the idle ranges, which need only their -inf fill, are
+// dealt to the remaining blocks, so none starts behind a scoring block; otherwise every block
+// takes the ranges j, j + N, ... of the whole order. (A separate instantiation: the walk costs
+// registers, which the one-range form keeps for occupancy.) Without the order (more rows than
+// threads), range L is (row L % Q, chunk L / Q).
+template <int D, bool FP8, int TPW, bool WALK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void index_scores_valid_kernel(
-    int B, int P, int Hi, int KP, int first_key, float scale, const uint16_t *__restrict__ q,
-    const float *__restrict__ w, const int32_t *__restrict__ row_seq,
+    int Q, int chunks, int B, int P, int Hi, int KP, int first_key, float scale,
+    const uint16_t *__restrict__ q, const float *__restrict__ w, const int32_t *__restrict__ row_seq,
     const int32_t *__restrict__ row_pos, const void *__restrict__ keys,
     const float *__restrict__ key_scales, const uint8_t *__restrict__ pool_valid,
     float *__restrict__ scores, uint8_t *__restrict__ cand) {
@@ -208,19 +218,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     __shared__ int item_s[2];
     __shared__ int seq_s[kThreads];
     __shared__ long long pos_s[kThreads];
-    const int Q = gridDim.x, chunks = gridDim.y;
-    int r = blockIdx.x, c = blockIdx.y;
-    int b;
-    long long pos;
-    if (Q <= kThreads && Q * chunks < (1 << 15)) {
-        const int t = threadIdx.x;
-        const int L = blockIdx.y * Q + blockIdx.x;
-        if (t == 0) item_s[0] = r, item_s[1] = c;  // (ordered before the finder by the scan)
+    const int total = Q * chunks;
+    const int N = gridDim.x;
+    const int j = blockIdx.x;
+    const int t = threadIdx.x;
+    // Range L of the block's walk: its row and chunk, with the row's geometry.
+    auto run = [&](int r, int c, int b, long long pos) {
+        const long long lim = row_pool_limit(b, pos, B, P, KP, first_key);
+        const int slot0 = c * kChunkV;
+        if (slot0 >= lim) {  // no candidate in the range (uniform over the block): the fill only
+            for (int s = slot0 + t; s < min(slot0 + kChunkV, P); s += kThreads) {
+                scores[(size_t)r * P + s] = -INFINITY;
+                cand[(size_t)r * P + s] = 0;
+            }
+            return;
+        }
+        score_range<D, FP8, TPW, kThreads>(r, b, pos, slot0, B, P, Hi, KP, first_key, scale, q, w,
+                                           keys, key_scales, pool_valid, scores, cand, q_s, w_s);
+    };
+    if (Q <= kThreads && total < (1 << 15)) {
         int act = 0;  // ranges of row t holding candidates
         if (t < Q) {
             const int bt = row_seq[t];
             const long long pt = row_pos[t];
-            seq_s[t] = bt;  // every row's geometry stays in LDS for the block's own row
+            seq_s[t] = bt;  // every row's geometry stays in LDS for the block's ranges
             pos_s[t] = pt;
             const long long lim = row_pool_limit(bt, pt, B, P, KP, first_key);
             act = (int)((lim + kChunkV - 1) / kChunkV);
@@ -228,25 +249,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         const int idle = t < Q ? chunks - act : 0;
         int tot;  // both counts in one scan (each sum is below Q * chunks < 2^15)
         const int pre = block_exclusive_scan<kThreads>(act | (idle << 15), scan_s, &tot);
-        const int pa = pre & 0x7fff, pi = pre >> 15, n_act = tot & 0x7fff;
-        if (t < Q) {
-            if (L < n_act) {
-                if (L >= pa && L < pa + act) item_s[0] = t, item_s[1] = L - pa;
-            } else if (L - n_act >= pi && L - n_act < pi + idle) {
-                item_s[0] = t, item_s[1] = act + (L - n_act - pi);
+        const int pa = pre & 0x7fff, pi = pre >> 15, A = tot & 0x7fff;
+        // Range L of the order: its row and chunk (the row's thread publishes them).
+        auto find = [&](int L) {
+            if (t < Q) {
+                if (L < A) {
+                    if (L >= pa && L < pa + act) item_s[0] = t, item_s[1] = L - pa;
+                } else if (L - A >= pi && L - A < pi + idle) {
+                    item_s[0] = t, item_s[1] = act + (L - A - pi);
+                }
+            }
+            __syncthreads();
+        };
+        if constexpr (!WALK) {
+            find(j);
+            const int r = min(max(item_s[0], 0), Q - 1);
+            const int c = min(max(item_s[1], 0), chunks - 1);
+            run(r, c, seq_s[r], pos_s[r]);
+        } else {
+            // The block's ranges: L0, L0 + step, ... below total.
+            int L0 = j, step = N;
+            const int idle_blocks = N - A, idle_ranges = total - A;
+            if (A < N && idle_ranges <= 4 * idle_blocks) {
+                if (j < A) step = total;  // its one range with candidates
+                else L0 = A + (j - A), step = idle_blocks;
+            }
+            for (int L = L0; L < total; L += step) {
+                if (L != L0) __syncthreads();  // the previous range is done with q_s, w_s and item_s
+                find(L);
+                const int r = min(max(item_s[0], 0), Q - 1);
+                const int c = min(max(item_s[1], 0), chunks - 1);
+                run(r, c, seq_s[r], pos_s[r]);
             }
         }
-        __syncthreads();
-        r = min(max(item_s[0], 0), Q - 1);
-        c = min(max(item_s[1], 0), chunks - 1);
-        b = seq_s[r];
-        pos = pos_s[r];
+    } else if constexpr (!WALK) {
+        run(j % Q, j / Q, row_seq[j % Q], row_pos[j % Q]);
     } else {
-        b = row_seq[r];
-        pos = row_pos[r];
+        for (int L = j; L < total; L += N) {
+            if (L != j) __syncthreads();  // the previous range is done with q_s and w_s
+            const int r = L % Q;
+            run(r, L / Q, row_seq[r], row_pos[r]);
+        }
     }
-    score_range<D, FP8, TPW, kThreads>(r, b, pos, c * kChunkV, B, P, Hi, KP, first_key, scale, q,
-                                       w, keys, key_scales, pool_valid, scores, cand, q_s, w_s);
 }
 
 // Rows that all read one sequence's keys (prefill: consecutive positions of one sequence), as
@@ -456,9 +500,38 @@ hipError_t launch_valid_d(int Q, int B, int P, int Hi, int KP, int first_key, fl
                           hipStream_t stream) {
     constexpr int chunk = (kThreads / kWave) * TPW * 32;
     const int chunks = (P + chunk - 1) / chunk;
-    hipLaunchKernelGGL((index_scores_valid_kernel<D, FP8, TPW>), dim3(Q, chunks), dim3(kThreads), 0,
-                       stream, B, P, Hi, KP, first_key, scale, q, w, row_seq, row_pos, keys,
-                       key_scales, pool_valid, scores, cand);
+    const long long total = (long long)Q * chunks;
+    if (total > INT32_MAX) return hipErrorInvalidValue;
+    // Blocks resident at once on this device, for each form (cached per device).
+    static std::mutex mu;
+    static int resident[64][2] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        if (resident[dev][0] == 0) {
+            int one = 0, walk = 0, cus = 0;
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &one, reinterpret_cast<const void *>(&index_scores_valid_kernel<D, FP8, TPW, false>), kThreads, 0);
+            if (e == hipSuccess)
+                e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                    &walk, reinterpret_cast<const void *>(&index_scores_valid_kernel<D, FP8, TPW, true>), kThreads, 0);
+            if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            if (e != hipSuccess) return e;
+            resident[dev][0] = std::max(1, one) * std::max(1, cus);
+            resident[dev][1] = std::max(1, walk) * std::max(1, cus);
+        }
+    }
+    if (total <= resident[dev][0])
+        hipLaunchKernelGGL((index_scores_valid_kernel<D, FP8, TPW, false>), dim3((int)total), dim3(kThreads), 0,
+                           stream, Q, chunks, B, P, Hi, KP, first_key, scale, q, w, row_seq, row_pos,
+                           keys, key_scales, pool_valid, scores, cand);
+    else
+        hipLaunchKernelGGL((index_scores_valid_kernel<D, FP8, TPW, true>), dim3(resident[dev][1]),
+                           dim3(kThreads), 0, stream, Q, chunks, B, P, Hi, KP, first_key, scale, q, w,
+                           row_seq, row_pos, keys, key_scales, pool_valid, scores, cand);
     return hipGetLastError();
 }
 
