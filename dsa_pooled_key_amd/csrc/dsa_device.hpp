@@ -135,6 +135,13 @@ __device__ __forceinline__ void dma4(const void *src, uint32_t lds_base) {
                  : "m0");
 }
 
+// A raw buffer resource over [base, base + bytes): accesses past the end are dropped (loads
+// return 0). Word 3 is the usual gfx9 setting for untyped access (32-bit data format, which
+// only typed accesses read; no swizzle, no thread-id offset).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
+
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)(p);
 }

@@ -70,6 +70,12 @@ constexpr int kPStride = kTile + 8;    // bf16 per P row (80 bytes: conflict-fre
 // acc[nt][8*i8 .. 8*i8 + 7] of lane `lane` of wave v.
 constexpr int kPartHeader = 256;
 constexpr int kPartBytes = kPartHeader + 32 * kC * 2;
+// Partials are stored with the sc0 and sc1 cache-policy bits (written through to the memory
+// side rather than held dirty in the writing XCD's L2): the main kernel's end then has little to
+// write back before the combine can start, and the combine, whose blocks run on any XCD, reads
+// them from there (45.6 against 46.4 us for the fp8_mixed_b32 step; streaming stores alone
+// gave 45.9).
+constexpr int kWriteThrough = 1 | 16;  // sc0 | sc1
 
 // Tile geometry per storage format. A tile is 32 rows; rows arrive by 16-byte-a-lane DMA and
 // keep their storage format in LDS. Chunk c (16 bytes) of row r sits at position c ^ swz(r);
@@ -636,22 +642,24 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
         }
     } else {
         uint8_t *part = reinterpret_cast<uint8_t *>(ws) + (((size_t)r * G + g) * parts + blockIdx.y) * kPartBytes;
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(part, kPartBytes);
         if (tid < 32) {
-            reinterpret_cast<float *>(part)[tid] = msum_s[tid];
-            reinterpret_cast<float *>(part)[32 + tid] = lsum_s[tid];
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, msum_s[tid]), rs, 4 * tid, 0,
+                                                  kWriteThrough);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lsum_s[tid]), rs, 128 + 4 * tid, 0,
+                                                  kWriteThrough);
         }
-        {  // a block without tokens writes its zero O too (sum 0), so the merge needs no test
-            u32x4 *po = reinterpret_cast<u32x4 *>(part + kPartHeader);
+        // a block without tokens writes its zero O too (sum 0), so the merge needs no test
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
+        for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                for (int i8 = 0; i8 < 2; ++i8) {
-                    const f32x16 &a = acc[nt];
-                    po[((v * 4 + nt) * 2 + i8) * kWave + lane] =
-                        u32x4{pack_bf16x2(a[8 * i8], a[8 * i8 + 1]), pack_bf16x2(a[8 * i8 + 2], a[8 * i8 + 3]),
-                              pack_bf16x2(a[8 * i8 + 4], a[8 * i8 + 5]), pack_bf16x2(a[8 * i8 + 6], a[8 * i8 + 7])};
-                }
-        }
+            for (int i8 = 0; i8 < 2; ++i8) {
+                const f32x16 &a = acc[nt];
+                const u32x4 vec{pack_bf16x2(a[8 * i8], a[8 * i8 + 1]), pack_bf16x2(a[8 * i8 + 2], a[8 * i8 + 3]),
+                                pack_bf16x2(a[8 * i8 + 4], a[8 * i8 + 5]), pack_bf16x2(a[8 * i8 + 6], a[8 * i8 + 7])};
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    vec, rs, kPartHeader + 16 * (((v * 4 + nt) * 2 + i8) * kWave + lane), 0, kWriteThrough);
+            }
     }
 }
 
@@ -744,7 +752,7 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const int H, const uin
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const int h = g * 32 + m_lo + (c & 3) + 8 * (c >> 2);
-        if (h < H) out[((size_t)r * H + h) * kC + ch] = o[c];
+        if (h < H) __builtin_nontemporal_store(o[c], &out[((size_t)r * H + h) * kC + ch]);  // read by a later kernel
     }
 }
 
