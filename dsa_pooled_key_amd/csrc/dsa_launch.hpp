@@ -92,6 +92,8 @@ struct MlaPlan {
     size_t ws_bytes; // partial results for parts > 1
 };
 MlaPlan plan_sparse_mla(int Q, int W, int H);
+// Compute units of the current device (queried once per device).
+hipError_t device_cu_count(int *cus);
 // Size of the fixed device scratch behind dsa_sparse_mla_decode_noalloc, and its address on
 // the current device (looked up once per device, then cached).
 constexpr size_t kMlaNoallocScratchBytes = DSA_MLA_NOALLOC_SCRATCH_BYTES;

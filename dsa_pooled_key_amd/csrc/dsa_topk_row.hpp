@@ -94,7 +94,7 @@ __device__ __forceinline__ void load_keys(int P, int vec, const float *__restric
 // with EXPAND, token_ids[r, 0..W). Key slot i stands for pool pool0 + i, or for pool ids[i]
 // when an id table (LDS, ascending over the slots that hold candidates) is given; ties go to
 // the lower slot either way. Called by all kThreads threads of the block.
-template <int KPT, bool EXPAND>
+template <int KPT, bool EXPAND, bool KEEP_BINS = (KPT <= 16)>
 __device__ __forceinline__ void select_row(int r, int P, int Kw, uint32_t (&key)[KPT],
                                            int32_t *__restrict__ sel, const ExpandArgs &ex,
                                            Smem &sm, int pool0 = 0,
@@ -156,8 +156,9 @@ __device__ __forceinline__ void select_row(int r, int P, int Kw, uint32_t (&key)
             const int bn = (int)((ordered_key_value(key) - smin) * inv);
             return bn < 0 ? 0 : (bn >= kBins ? kBins - 1 : bn);
         };
-        // Up to 16 keys a thread, their bins stay in registers for the membership test below.
-        constexpr bool kKeepBins = KPT <= 16;
+        // With KEEP_BINS the bins stay in registers for the membership test below; otherwise
+        // they are computed again there (fewer registers).
+        constexpr bool kKeepBins = KEEP_BINS;
         int bn[kKeepBins ? KPT : 1];
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {

@@ -518,7 +518,7 @@ hipError_t launch_valid_d(int Q, int B, int P, int Hi, int KP, int first_key, fl
             if (e == hipSuccess)
                 e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
                     &walk, reinterpret_cast<const void *>(&index_scores_valid_kernel<D, FP8, TPW, true>), kThreads, 0);
-            if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            if (e == hipSuccess) e = device_cu_count(&cus);
             if (e != hipSuccess) return e;
             resident[dev][0] = std::max(1, one) * std::max(1, cus);
             resident[dev][1] = std::max(1, walk) * std::max(1, cus);

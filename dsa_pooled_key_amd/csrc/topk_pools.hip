@@ -7,6 +7,8 @@
 // loads the row's keys and runs the selection of dsa_topk_row.hpp; the fused variant also
 // writes the row's token ids exactly as expand_selection does, so the selection never goes
 // back to memory to be read again.
+#include <mutex>
+
 #include "dsa_device.hpp"
 #include "dsa_launch.hpp"
 #include "dsa_topk_row.hpp"
@@ -16,19 +18,21 @@ namespace {
 
 using namespace topk;
 
-template <int KPT, bool EXPAND>
-__global__ __launch_bounds__(kThreads) void topk_pools_kernel(int P, int Kw, int vec,
-                                                              const float *__restrict__ scores,
-                                                              const uint8_t *__restrict__ cand,
-                                                              int32_t *__restrict__ sel,
-                                                              ExpandArgs ex) {
+// PAIR: the form for more rows than compute units, held to 64 registers (the keys' value bins
+// are computed again for the membership test instead of kept), so that two 1024-thread blocks
+// share a CU (71.7 against 91.6 us for the 2,048 rows of prefill_2048_64k). With fewer rows a
+// block's latency is what counts, and the unconstrained form is faster (10.2 against 11.9 us
+// for fp8_mixed_b32's 32 rows).
+template <int KPT, bool EXPAND, bool PAIR>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PAIR ? 8 : 1))) void topk_pools_kernel(
+    int P, int Kw, int vec, const float *__restrict__ scores, const uint8_t *__restrict__ cand,
+    int32_t *__restrict__ sel, ExpandArgs ex) {
     __shared__ Smem sm;
     const int r = blockIdx.x;
-    const int tid = threadIdx.x;
 
     uint32_t key[KPT];
     load_keys<KPT>(P, vec, scores + (size_t)r * P, cand + (size_t)r * P, key);
-    select_row<KPT, EXPAND>(r, P, Kw, key, sel, ex, sm);
+    select_row<KPT, EXPAND, !PAIR && KPT <= 16>(r, P, Kw, key, sel, ex, sm);
 }
 
 // Two stages for rows that are few and long, which a block each would leave most of the chip
@@ -97,12 +101,26 @@ hipError_t launch_kpt(int Q, int P, int Kw, const float *scores, const uint8_t *
     const int vec = (KPT >= 16 ? (P & 15) == 0 && (reinterpret_cast<uintptr_t>(cand) & 15) == 0
                                 : (P & 3) == 0 && (reinterpret_cast<uintptr_t>(cand) & 3) == 0) &&
                     (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
-    if (ex)
-        hipLaunchKernelGGL((topk_pools_kernel<KPT, true>), dim3(Q), dim3(kThreads), 0, stream, P,
-                           Kw, vec, scores, cand, sel, *ex);
+    const ExpandArgs exa = ex ? *ex : ExpandArgs{};
+    bool pair = false;
+    if constexpr (KPT == 16) {  // the only width whose 64-register form does not spill
+        int cus = 0;
+        const hipError_t e = device_cu_count(&cus);
+        if (e != hipSuccess) return e;
+        pair = Q > cus;
+    }
+    if (ex && pair)
+        hipLaunchKernelGGL((topk_pools_kernel<KPT, true, true>), dim3(Q), dim3(kThreads), 0, stream, P,
+                           Kw, vec, scores, cand, sel, exa);
+    else if (ex)
+        hipLaunchKernelGGL((topk_pools_kernel<KPT, true, false>), dim3(Q), dim3(kThreads), 0, stream, P,
+                           Kw, vec, scores, cand, sel, exa);
+    else if (pair)
+        hipLaunchKernelGGL((topk_pools_kernel<KPT, false, true>), dim3(Q), dim3(kThreads), 0, stream, P,
+                           Kw, vec, scores, cand, sel, exa);
     else
-        hipLaunchKernelGGL((topk_pools_kernel<KPT, false>), dim3(Q), dim3(kThreads), 0, stream, P,
-                           Kw, vec, scores, cand, sel, ExpandArgs{});
+        hipLaunchKernelGGL((topk_pools_kernel<KPT, false, false>), dim3(Q), dim3(kThreads), 0, stream, P,
+                           Kw, vec, scores, cand, sel, exa);
     return hipGetLastError();
 }
 
@@ -152,6 +170,25 @@ hipError_t launch_any(int Q, int P, int Kw, const float *scores, const uint8_t *
 }
 
 }  // namespace
+
+hipError_t device_cu_count(int *cus) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static int count[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (count[dev] == 0) {
+        int n = 0;
+        e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        count[dev] = n > 0 ? n : 1;
+    }
+    *cus = count[dev];
+    return hipSuccess;
+}
 
 size_t topk_workspace_bytes(int Q, int P, int Kw) {
     const int nseg = topk_segments(Q, P, Kw);
