@@ -461,7 +461,7 @@ def run_cpu_baseline(di, sample_every: int, min_seconds: float = 10.0, max_passe
                       f"whole decode chain, {passes} passes, {dt:.1f} s wall"}
 
 
-def run_cpu_baseline_rows(di, n_rows: int, seed: int, min_seconds: float = 10.0, max_passes: int = 4):
+def run_cpu_baseline_rows(di, n_rows: int, seed: int, min_seconds: float = 10.0, max_passes: int = 16):
     """The oracle's whole chain on a seeded random subsample of n_rows query rows (prefill:
     rows of one sequence), repeated until min_seconds have passed; rows/s."""
     import oracle
