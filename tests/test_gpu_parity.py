@@ -191,6 +191,43 @@ def test_compact_index_scores_equals_the_two_calls(name):
     assert np.array_equal(s1.cpu().numpy().view(np.uint32), s2.cpu().numpy().view(np.uint32))
 
 
+@pytest.mark.parametrize("name", ["decode_b8_32k", "ragged_fp8"])
+def test_compact_index_scores_more_rows_than_threads(name):
+    """300 rows over the workload's sequences (rows drawn with replacement, positions redrawn
+    below each sequence's length): more rows than a block has threads, so the ranges are not
+    reordered, and on decode_b8_32k (300 x 64 ranges) the grid walks them. Every slot equals
+    compact_pools + index_scores bit for bit; sampled rows match the oracle."""
+    di, x, _, _ = case(name)
+    wl = di.wl
+    cfg = config_for(wl)
+    rng = np.random.default_rng(7)
+    R = 300
+    src = rng.integers(0, wl.Q, size=R)
+    row_seq = di.row_seq[src].astype(np.int32)
+    row_pos = (rng.random(R) * di.lengths[row_seq]).astype(np.int32)
+    q, w = _dev(di.q[src].view(np.int16)).view(torch.bfloat16), _dev(di.w[src])
+    rs_d, rp_d = _dev(row_seq), _dev(row_pos)
+    s1, c1 = dsa.compact_index_scores(cfg, q, w, rs_d, rp_d, x.keys, x.pool_valid,
+                                      first_key=wl.first_key, scale=di.scale,
+                                      key_scales=x.key_scales)
+    ids = torch.empty((wl.B, wl.pools), dtype=torch.int32, device=x.q.device)
+    nv = torch.empty((wl.B,), dtype=torch.int32, device=x.q.device)
+    dsa.compact_pools(x.pool_valid, ids, nv)
+    s2, c2 = dsa.index_scores(cfg, q, w, rs_d, rp_d, x.keys, ids, nv, first_key=wl.first_key,
+                              scale=di.scale, key_scales=x.key_scales)
+    assert np.array_equal(c1.cpu().numpy(), c2.cpu().numpy())
+    assert np.array_equal(s1.cpu().numpy().view(np.uint32), s2.cpu().numpy().view(np.uint32))
+    rows = np.unique(np.r_[0, rng.choice(R, size=6, replace=False), R - 1])
+    ids_o, nv_o = oracle.compact_pools(di.pool_valid)
+    rs, rc = oracle.index_scores(di.q[src][rows], di.w[src][rows], row_seq[rows], row_pos[rows],
+                                 di.keys, ids_o, nv_o, kpool=wl.kpool, first_key=wl.first_key,
+                                 scale=di.scale, key_scales=di.key_scales)
+    gs, gc = s1.cpu().numpy()[rows], c1.cpu().numpy()[rows]
+    assert np.array_equal(gc, rc)
+    _check_scores(gs, rs, rc, _bound(di, rows, q=di.q[src][rows], w=di.w[src][rows],
+                                     row_seq=row_seq[rows]))
+
+
 @pytest.mark.parametrize("name", ["ragged_prefill", "ragged_fp8"])
 def test_compact_index_scores_rows_of_one_sequence(name):
     """Many rows over one sequence take the row-blocked scorer (8 rows x 128 pools a block):
