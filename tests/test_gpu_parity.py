@@ -356,6 +356,45 @@ def test_topk_ties_signs_and_row_lengths(P, kw, seed):
     assert np.array_equal(ftok.cpu().numpy(), tok_ref)
 
 
+@pytest.mark.parametrize("P,kw", [(16384, 512), (12000, 300)])
+def test_topk_more_rows_than_compute_units(P, kw):
+    """300 rows of 16 keys a thread, more rows than compute units: the 64-register form that
+    puts two blocks on a CU. Rows cycle through heavy ties, signed zeros, tiny magnitudes,
+    all-negative scores, fewer candidates than kw, none, and plain normal scores; every row
+    bit-exact against the oracle, plain and fused with expansion."""
+    rng = np.random.default_rng(11)
+    Q = 300
+    scores = rng.standard_normal((Q, P)).astype(np.float32)
+    cand = (rng.random((Q, P)) < 0.8).astype(np.uint8)
+    for r in range(0, Q, 7):
+        kind = (r // 7) % 6
+        if kind == 0:
+            scores[r] = rng.integers(-40, 41, P) / 8.0
+        elif kind == 1:
+            scores[r] = 0.0
+            scores[r, ::3] = -0.0
+        elif kind == 2:
+            scores[r] = rng.standard_normal(P) * 1e-30
+        elif kind == 3:
+            scores[r] = -np.abs(rng.standard_normal(P))
+        elif kind == 4:
+            cand[r] = 0
+            cand[r, : kw // 2] = 1
+        else:
+            cand[r] = 0
+    scores[cand == 0] = -np.inf
+    cfg = dsa.Config.make(index_heads=32, index_head_dim=128, index_kpool=1, index_topk=kw,
+                          heads=32)
+    ref = oracle.topk_pools(scores, cand, kw)
+    got = dsa.topk_pools(cfg, _dev(scores), _dev(cand)).cpu().numpy()
+    assert np.array_equal(got, ref)
+    zeros = _dev(np.zeros(Q, np.int32))
+    fsel, ftok = dsa.topk_expand(cfg, _dev(scores), _dev(cand), zeros, zeros,
+                                 _dev(np.ones((1, P), np.uint8)), S=P, first_key=0)
+    assert np.array_equal(fsel.cpu().numpy(), ref)
+    assert np.array_equal(ftok.cpu().numpy(), ref)
+
+
 @pytest.mark.parametrize("P,kw,seed", [(8192, 512, 40), (16384, 512, 41), (16384, 100, 42),
                                        (32768, 512, 43), (32768, 2048, 44)])
 def test_topk_rows_of_many_candidates_a_thread(P, kw, seed):
