@@ -522,6 +522,65 @@ def stream_read_line(replays: int = 10):
             "frac_of_nominal_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
+def mfma_rate_line(blocks: int = 1024, iters: int = 2048, launches: int = 5):
+    """The matrix units' dense rate on this GPU for the MFMA shapes the kernels use: the
+    library's MFMA loop (4 independent chains a wave, 4 waves a block, 4 blocks a CU), HIP
+    events around repeated launches."""
+    import torch
+
+    from dsa_pooled_key_amd import binding as dsa
+
+    out = torch.empty((blocks * 256,), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.Stream()
+    res = {}
+    with torch.cuda.stream(stream):
+        for kind, (name, _) in dsa.MFMA_RATE_SHAPES.items():
+            for _ in range(2):
+                dsa.mfma_rate(kind, blocks, iters, out)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            flop = 0
+            for _ in range(launches):
+                flop += dsa.mfma_rate(kind, blocks, iters, out)
+            b.record(stream)
+            b.synchronize()
+            tfs = flop / (a.elapsed_time(b) * 1e-3) / 1e12
+            res[name] = round(tfs, 1)
+            log(f"MFMA {name}: {tfs:.0f} TFLOP/s")
+    return {"TFLOPs": res, "blocks": blocks, "waves_per_block": 4, "chains_per_wave": 4,
+            "bf16_frac_of_nominal_peak": round(max(res[dsa.MFMA_RATE_SHAPES[0][0]],
+                                                   res[dsa.MFMA_RATE_SHAPES[1][0]]) / PEAK_BF16_TFS, 4)}
+
+
+def launch_gap_line(launches: int = 200, replays: int = 5):
+    """The gap between dependent launches in a replayed graph: a graph of empty kernels on one
+    stream (1 block, and 256 blocks), HIP events around the replays."""
+    import torch
+
+    from dsa_pooled_key_amd import binding as dsa
+
+    stream = torch.cuda.Stream()
+    res = {}
+    for blocks in (1, 256):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(launches):
+                dsa.empty_launch(blocks)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        with torch.cuda.stream(stream):
+            for _ in range(replays):
+                g.replay()
+        b.record(stream)
+        b.synchronize()
+        res[f"{blocks}_block{'s' if blocks > 1 else ''}"] = round(a.elapsed_time(b) * 1e3 / (replays * launches), 3)
+        del g
+    log(f"graph launch gap: {res} us a launch")
+    return {"us_per_launch": res, "launches_per_graph": launches}
+
+
 # ---------------------------------------------------------------- main
 
 def run_eager(args):
@@ -609,6 +668,8 @@ def main():
 
     res = run_gpu(args)
     stream = stream_read_line()
+    mfma = mfma_rate_line()
+    gap = launch_gap_line()
     di, alg, ms = res["di"], res["alg"], res["ms_step"]
     wl = di.wl
     value = wl.Q / (ms * 1e-3)
@@ -673,6 +734,8 @@ def main():
             "frac_of_measured_stream_read": round(step_gbs / stream["GBs"], 4),
         },
         "hbm_stream_read": stream,
+        "mfma_measured": mfma,
+        "graph_launch_gap": gap,
         "stage_us": {k: round(v, 3) for k, v in res["stage_us"].items()},
         "kpool_compress": {
             "tokens_per_s": round(kp["tokens"] / (kp["us"] * 1e-6), 1),
@@ -704,6 +767,10 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if "prefill" in extra:
+        pr = extra["prefill"]["roofline"]
+        bf16 = max(v for k, v in mfma["TFLOPs"].items() if "bf16" in k)
+        pr["frac_of_measured_mfma"] = round(pr["achieved"] / bf16, 4)
     line.update(extra)
     print(json.dumps(line), flush=True)
 

@@ -39,7 +39,7 @@ EXPORTED = [
     "dsa_compact_index_scores",
     "dsa_topk_workspace", "dsa_topk_pools_workspace", "dsa_topk_pools", "dsa_expand_selection", "dsa_topk_expand",
     "dsa_sparse_mla_decode_workspace",
-    "dsa_sparse_mla_decode", "dsa_sparse_mla_decode_noalloc", "dsa_stream_read", "dsa_absorb_q", "dsa_absorb_o", "dsa_f32_to_bf16_rne",
+    "dsa_sparse_mla_decode", "dsa_sparse_mla_decode_noalloc", "dsa_stream_read", "dsa_empty_launch", "dsa_mfma_rate", "dsa_absorb_q", "dsa_absorb_o", "dsa_f32_to_bf16_rne",
 ]
 
 
@@ -112,6 +112,8 @@ def lib():
             "dsa_sparse_mla_decode_noalloc": ([_CFG, _I, _I, _I, _F, _P, _P, _P, _P, _I, _P,
                                                _I64, _I, _P, _I, _I, _P, _P, _P], _I),
             "dsa_stream_read": ([_P, _SZ, _P, _P], _I),
+            "dsa_empty_launch": ([_I, _P], _I),
+            "dsa_mfma_rate": ([_I, _I, _I, _P, _P], _I),
             "dsa_absorb_q": ([_CFG, _P, _SZ, _P, _SZ, _I, _I, _P, _SZ], _I),
             "dsa_absorb_o": ([_CFG, _P, _SZ, _P, _SZ, _I, _I, _P, _SZ], _I),
             "dsa_f32_to_bf16_rne": ([_P, _P, _SZ], None),
@@ -655,3 +657,23 @@ def stream_read(buf, sink=None):
         sink = torch.zeros((1,), dtype=torch.int32, device=buf.device)
     _check(lib().dsa_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(buf)))
     return sink
+
+
+def empty_launch(blocks: int = 1, stream=None):
+    """Measurement only: one launch of a kernel that does nothing (blocks of 64 threads)."""
+    st = stream if stream is not None else torch.cuda.current_stream()
+    _check(lib().dsa_empty_launch(int(blocks), ctypes.c_void_p(st.cuda_stream)))
+
+
+# Floating-point operations of one MFMA of each dsa_mfma_rate shape (2*M*N*K).
+MFMA_RATE_SHAPES = {0: ("v_mfma_f32_32x32x16_bf16", 2 * 32 * 32 * 16),
+                    1: ("v_mfma_f32_16x16x32_bf16", 2 * 16 * 16 * 32),
+                    2: ("v_mfma_scale_f32_16x16x128_f8f6f4 (e4m3)", 2 * 16 * 16 * 128)}
+
+
+def mfma_rate(kind: int, blocks: int, iters: int, out):
+    """Measurement only: blocks x 4 waves x iters rounds of 4 independent MFMAs of one shape
+    (MFMA_RATE_SHAPES); out: [blocks * 256] f32 on the device. Returns the flop count."""
+    _dev(out, "out", (torch.float32,), (blocks * 256,))
+    _check(lib().dsa_mfma_rate(int(kind), int(blocks), int(iters), _ptr(out), _stream(out)))
+    return blocks * 4 * iters * 4 * MFMA_RATE_SHAPES[kind][1]

@@ -22,18 +22,23 @@ ARCH = "gfx950"
 
 KERNELS = ["kpool_compress.hip", "cache_update.hip", "compact_pools.hip", "index_scores.hip",
            "topk_pools.hip",
-           "expand_selection.hip", "sparse_mla_decode.hip", "masked_attn.hip", "stream_read.hip"]
+           "expand_selection.hip", "sparse_mla_decode.hip", "masked_attn.hip", "measure.hip"]
 HOST = ["dsa_api.cpp", "absorb.cpp"]
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
           "-packed-fp32-ops", "-ffp-contract=fast"]
 HOST_ONLY = ["-ffp-contract=off"]
+# Per-file additions. The MFMA-rate measurement keeps MFMA accumulators in the VGPR form (the
+# form the production kernels get under their register pressure): in the accumulator-register
+# form the compiler copies a 16x16 chain's result back every round, so the loop would measure
+# those copies.
+EXTRA = {"measure.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    flags = COMMON + (DEVICE if src.endswith(".hip") else HOST_ONLY)
+    flags = COMMON + (DEVICE if src.endswith(".hip") else HOST_ONLY) + EXTRA.get(src, [])
     cmd = [HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)

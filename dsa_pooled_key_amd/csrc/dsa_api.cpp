@@ -555,4 +555,19 @@ int dsa_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s
     return hip_status(dsa::launch_stream_read(buf, bytes, sink, 2048, stream), "stream_read launch");
 }
 
+int dsa_empty_launch(int blocks, hipStream_t stream) {
+    clear_error();
+    if (blocks < 1 || blocks > 65535)
+        return set_error(DSA_ERR_BAD_SIZE, "empty_launch: blocks must be in 1..65535 (got %d)", blocks);
+    return hip_status(dsa::launch_empty(blocks, stream), "empty launch");
+}
+
+int dsa_mfma_rate(int kind, int blocks, int iters, float *out, hipStream_t stream) {
+    clear_error();
+    if (kind < 0 || kind > 2 || blocks < 1 || blocks > 65535 || iters < 2 || iters % 2 != 0)
+        return set_error(DSA_ERR_BAD_SIZE, "mfma_rate: kind 0..2, blocks 1..65535, iters even and >= 2");
+    if (!out) return set_error(DSA_ERR_NULL_ARG, "mfma_rate: out is NULL");
+    return hip_status(dsa::launch_mfma_rate(kind, blocks, iters, out, stream), "mfma_rate launch");
+}
+
 }  // extern "C"

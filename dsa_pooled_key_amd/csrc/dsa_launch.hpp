@@ -108,5 +108,7 @@ hipError_t launch_sparse_mla(const MlaPlan &plan, int Q, int W, int H, int B, fl
 // Measurement only (stream_read.hip): every 16-byte word of buf read once; sink gets the XOR.
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int blocks,
                               hipStream_t stream);
+hipError_t launch_empty(int blocks, hipStream_t stream);
+hipError_t launch_mfma_rate(int kind, int blocks, int iters, float *out, hipStream_t stream);
 
 }  // namespace dsa

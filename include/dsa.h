@@ -373,6 +373,20 @@ void dsa_f32_to_bf16_rne(const float *src, uint16_t *dst, size_t n);
  * kernels' bandwidth is reported against, beside the nominal peak. */
 int dsa_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
 
+/* Not a step of the method: launches a kernel of `blocks` (1 .. 65535) blocks of 64 threads
+ * that does nothing. A graph of many such launches, replayed, gives the gap between dependent
+ * launches on the stream. DSA_ERR_BAD_SIZE for blocks out of range. */
+int dsa_empty_launch(int blocks, hipStream_t stream);
+
+/* Not a step of the method: the matrix units' dense rate. Each of the `blocks` (1 .. 65535)
+ * blocks has 4 waves; each wave runs `iters` (even, >= 2) rounds of 4 independent MFMAs of one shape:
+ * kind 0 = v_mfma_f32_32x32x16_bf16, 1 = v_mfma_f32_16x16x32_bf16, 2 =
+ * v_mfma_scale_f32_16x16x128_f8f6f4 with e4m3 operands. One launch performs
+ * blocks * 4 * iters * 4 * 2*M*N*K floating-point operations (M*N*K = 16384 for kinds 0 and 1,
+ * 32768 for kind 2). out (device, blocks * 256 floats) receives one sum per thread so the work
+ * cannot be dropped. DSA_ERR_BAD_SIZE for an argument out of range, DSA_ERR_NULL_ARG for out. */
+int dsa_mfma_rate(int kind, int blocks, int iters, float *out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -150,6 +150,21 @@ _NULL = None
 _FAKE = ctypes.c_void_p(0x10000)   # never dereferenced: every call below is refused first
 
 
+def test_measurement_entry_points_refuse_bad_arguments():
+    """The measurement-only calls check their arguments before any launch."""
+    L = dsa.lib()
+    assert L.dsa_empty_launch(0, _NULL) == -2
+    assert L.dsa_empty_launch(65536, _NULL) == -2
+    assert L.dsa_mfma_rate(3, 1, 2, _FAKE, _NULL) == -2      # no such shape
+    assert L.dsa_mfma_rate(0, 0, 2, _FAKE, _NULL) == -2      # no blocks
+    assert L.dsa_mfma_rate(1, 1, 3, _FAKE, _NULL) == -2      # odd round count
+    assert "even" in dsa.last_error()
+    assert L.dsa_mfma_rate(2, 1, 2, _NULL, _NULL) == -1      # no output
+    assert L.dsa_stream_read(_FAKE, 24, _FAKE, _NULL) == -2  # not a multiple of 16 bytes
+    assert L.dsa_stream_read(_NULL, 32, _FAKE, _NULL) == -1
+    assert L.dsa_stream_read(_NULL, 0, _NULL, _NULL) == 0     # nothing to read
+
+
 def test_refusals_return_codes_without_launching():
     L = dsa.lib()
     cfg = _cfg()
