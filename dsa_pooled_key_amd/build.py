@@ -3,6 +3,10 @@
 Each source under csrc/ is compiled to an object with its own flags and the objects are linked
 into dsa_pooled_key_amd/libdsa.so. Device code is compiled with packed-fp32 instructions
 disabled; the host weight transforms with FMA contraction disabled.
+
+`python -m dsa_pooled_key_amd.build --trace` builds libdsa_trace.so beside it instead: the
+same sources with DSA_PHASE_TRACE defined, so the decode-step kernels record per-block phase
+timestamps (dsa_phase.hpp) for phase_trace.py. The product library never has them.
 """
 from __future__ import annotations
 
@@ -36,9 +40,15 @@ HOST_ONLY = ["-ffp-contract=off"]
 EXTRA = {"measure.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+TRACE_LIB_PATH = os.path.join(HERE, "libdsa_trace.so")
+TRACE_BUILD = os.path.join(ROOT, "_build_trace")
+
+
+def _compile(src: str, verbose: bool, trace: bool = False) -> str:
+    obj = os.path.join(TRACE_BUILD if trace else BUILD, os.path.basename(src) + ".o")
     flags = COMMON + (DEVICE if src.endswith(".hip") else HOST_ONLY) + EXTRA.get(src, [])
+    if trace and src.endswith(".hip"):
+        flags = flags + ["-DDSA_PHASE_TRACE"]
     cmd = [HIPCC] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -50,20 +60,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build_library(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build_library(verbose: bool = False, jobs: int = 8, trace: bool = False) -> str:
+    """Compiles every source and links the library; returns its path (trace: the
+    phase-timestamp library, libdsa_trace.so)."""
+    out = TRACE_LIB_PATH if trace else LIB_PATH
+    os.makedirs(TRACE_BUILD if trace else BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), KERNELS + HOST))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, trace), KERNELS + HOST))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build_library(verbose="-v" in sys.argv))
+    print(build_library(verbose="-v" in sys.argv, trace="--trace" in sys.argv))

@@ -17,6 +17,7 @@
 #pragma once
 
 #include "dsa_device.hpp"
+#include "dsa_phase.hpp"
 
 namespace dsa {
 
@@ -82,6 +83,7 @@ __device__ __forceinline__ void score_range(
     const float wv = tid < 32 && tid < Hi ? w[(size_t)r * Hi + tid] : 0.0f;
     const long long lim = row_pool_limit(b, pos, B, P, KP, first_key);
 
+    DSA_PHASE(0, 1);  // range known, query requested
     // The validity flags of this lane's slots, then (round trip 2) their keys. The
     // flags sit under one branch that is uniform over the wave (a lane past the row's limit
     // reads the last flag in range and drops it), so they are requested together: under a
@@ -134,6 +136,7 @@ __device__ __forceinline__ void score_range(
     }
     if (tid < 32) w_s[tid] = wv;
     __syncthreads();
+    DSA_PHASE(0, 2);  // query and flags landed, query staged
 
     float wr[16];
 #pragma unroll
@@ -158,6 +161,7 @@ __device__ __forceinline__ void score_range(
             }
             const float f = scale * ksc[t];
             tot = f * add_xor32(relu_weighted(acc, wr, f));
+            if (t == 0) DSA_PHASE(0, 3);  // keys landed, first tile scored
             if (tot == 0.0f) tot = 0.0f;
         }
         if (half == 0 && slot[t] < P) {

@@ -17,6 +17,7 @@
 #pragma once
 
 #include "dsa_device.hpp"
+#include "dsa_phase.hpp"
 
 namespace dsa {
 namespace topk {
@@ -126,6 +127,7 @@ __device__ __forceinline__ void select_row(int r, int P, int Kw, uint32_t (&key)
         red3[1][wave] = kmax;
         red3[2][wave] = kmin;
     }
+    DSA_PHASE(1, 1);  // keys loaded and reduced in the wave
     if (tid == 0) n_mem = 0;
     for (int i = tid; i < kBins; i += kThreads) bins[i] = 0u;  // used only past this barrier
     __syncthreads();
@@ -138,6 +140,7 @@ __device__ __forceinline__ void select_row(int r, int P, int Kw, uint32_t (&key)
         kmax = red3[1][w] > kmax ? red3[1][w] : kmax;
         kmin = red3[2][w] < kmin ? red3[2][w] : kmin;
     }
+    DSA_PHASE(1, 2);  // block reduction done
     const int take = n_cand < Kw ? n_cand : Kw;
 
     uint32_t thr = 0u;  // take every key > thr, plus `need` of the keys == thr
@@ -196,6 +199,7 @@ __device__ __forceinline__ void select_row(int r, int P, int Kw, uint32_t (&key)
             }
         }
         __syncthreads();
+        DSA_PHASE(1, 3);  // histogram scanned, cutoff bin known
         const int bstar = (int)pick[0];
         int k = Kw - (int)pick[1];  // rank of the cutoff inside b*
         const int members = (int)pick[2];
@@ -281,6 +285,7 @@ __device__ __forceinline__ void select_row(int r, int P, int Kw, uint32_t (&key)
         }
     }
 
+    DSA_PHASE(1, 4);  // cutoff key known
     // Output positions in pool order: every key above thr, plus the first `need` keys equal to
     // it (the tie scan is skipped when all of them are taken).
     int gt = 0, eq = 0;
@@ -329,6 +334,7 @@ __device__ __forceinline__ void select_row(int r, int P, int Kw, uint32_t (&key)
             }
         }
     };
+    DSA_PHASE(1, 5);  // output positions known
     auto pool_of = [&](int i) { return ids != nullptr ? ids[base + i] : pool0 + base + i; };
     if (Kw <= kStageSel) {
         // The ids go to LDS at their positions; after one barrier thread j writes position j,
@@ -351,6 +357,7 @@ __device__ __forceinline__ void select_row(int r, int P, int Kw, uint32_t (&key)
         }
         for (int i = take + tid; i < Kw; i += kThreads) orow[i] = -1;
     }
+    DSA_PHASE(1, 6);  // selection written
     if constexpr (EXPAND) {
         // The remaining token slots (as expand_selection): -1 up to topk, then the tail tokens
         // after the last whole pool up to row_pos, each only if valid.

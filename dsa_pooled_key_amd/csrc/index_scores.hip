@@ -29,6 +29,10 @@
 
 #include "dsa_device.hpp"
 #include "dsa_launch.hpp"
+#include "dsa_phase.hpp"
+
+DSA_PHASE_TABLE(scores)
+
 #include "dsa_score_range.hpp"
 
 namespace dsa {
@@ -218,6 +222,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     __shared__ int item_s[2];
     __shared__ int seq_s[kThreads];
     __shared__ long long pos_s[kThreads];
+    DSA_PHASE(0, 0);  // block start
     const int total = Q * chunks;
     const int N = gridDim.x;
     const int j = blockIdx.x;
@@ -235,6 +240,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         }
         score_range<D, FP8, TPW, kThreads>(r, b, pos, slot0, B, P, Hi, KP, first_key, scale, q, w,
                                            keys, key_scales, pool_valid, scores, cand, q_s, w_s);
+        DSA_PHASE(0, 4);  // range scored, stores issued
     };
     if (Q <= kThreads && total < (1 << 15)) {
         int act = 0;  // ranges of row t holding candidates

@@ -27,6 +27,9 @@
 
 #include "dsa_device.hpp"
 #include "dsa_launch.hpp"
+#include "dsa_phase.hpp"
+
+DSA_PHASE_TABLE(mla)
 
 namespace dsa {
 
@@ -148,6 +151,7 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
     __shared__ int rescale_all[TEAMS][2];
     __shared__ __attribute__((aligned(16))) float mf_s[TEAMS][32];  // per-head merge factors
 
+    DSA_PHASE(2, 0);  // block start
     const int r = blockIdx.x;
     const int tm = threadIdx.x / kThreads;  // team
     const int split = blockIdx.y * TEAMS + tm;
@@ -265,6 +269,7 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
     // the chip-wide burst of first tiles each team's tile 0 then lands before any tile 1
     // (fp8 issues tile 1 after the prologue barrier, 29.9 against 30.3 us for the stage on
     // fp8_mixed_b32).
+    DSA_PHASE(2, 1);  // token ids and latent rows resolved
     if constexpr (FP8) stage_q();  // the query rows with tile 0
     const int pre = kv_rows > 0 ? min(n_ptiles, 1) : 0;
     for (int t = 0; t < pre; ++t) issue(t);
@@ -277,6 +282,7 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
     if (FP8 || pre == 0) wait_vm<0>();
     else wait_vm<G_::kLoadsT>();
     __syncthreads();
+    DSA_PHASE(2, 2);  // query rows and tile 0 landed, prologue barrier passed
     const int last = max(max(last_w[0], last_w[1]), max(last_w[2], last_w[3]));
     const int n_tiles = (last + kTile) / kTile;  // through the last slot with a token
     // The teams step through n_iter tiles together, since the barriers are the block's; a team
@@ -497,6 +503,7 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
             }
             lds_barrier();  // C
         }
+        DSA_PHASE(2, 3);  // first tile done
         // Iteration t, before B: every LDS operand of the refill, of tile t-1's P and of the
         // scores of tile t is requested before the first is used, so their latencies overlap
         // one another and the MFMA work instead of adding up.
@@ -546,6 +553,7 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
             }
         }
         if (n_tiles > 0 && n_tiles == n_iter) products(n_tiles - 1);
+        DSA_PHASE(2, 4);  // every tile done
     } else {
         // bf16: one tile in flight (two 32 KiB stages); barrier A opens each tile once it is
         // resident and the stage of tile t-1 is free for tile t+1 (for t = 0: the query rows
@@ -564,6 +572,7 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
             lds_barrier();  // C
             if (act) products(t);
         }
+        DSA_PHASE(2, 4);  // every tile done
     }
 
     wait_vm<0>();  // a tile fetched ahead but past the last token still lands in LDS first
@@ -622,6 +631,7 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
         }
     }
 
+    DSA_PHASE(2, 5);  // teams merged
     // The block's result: out and lse when it covers the whole row, else partial blockIdx.y.
     const int parts = gridDim.y;
     if (parts == 1) {
@@ -661,6 +671,7 @@ __global__ __launch_bounds__(kThreads * TEAMS) __attribute__((amdgpu_waves_per_e
                     vec, rs, kPartHeader + 16 * (((v * 4 + nt) * 2 + i8) * kWave + lane), 0, kWriteThrough);
             }
     }
+    DSA_PHASE(2, 6);  // result stores issued
 }
 
 // Merge the split partials of one (row, head group): block z = 4v + nt covers channels
@@ -675,6 +686,7 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const int H, const uin
                                                           float *__restrict__ lse) {
     __shared__ __attribute__((aligned(16))) float wgt[NP][32];
     __shared__ float red4[4][32];
+    DSA_PHASE(3, 0);
     const int r = blockIdx.x;
     const int g = blockIdx.y;
     const int G = gridDim.y;
@@ -754,6 +766,7 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(const int H, const uin
         const int h = g * 32 + m_lo + (c & 3) + 8 * (c >> 2);
         if (h < H) __builtin_nontemporal_store(o[c], &out[((size_t)r * H + h) * kC + ch]);  // read by a later kernel
     }
+    DSA_PHASE(3, 1);
 }
 
 template <int NP>

@@ -11,6 +11,10 @@
 
 #include "dsa_device.hpp"
 #include "dsa_launch.hpp"
+#include "dsa_phase.hpp"
+
+DSA_PHASE_TABLE(topk)
+
 #include "dsa_topk_row.hpp"
 
 namespace dsa {
@@ -30,9 +34,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PAIR ?
     __shared__ Smem sm;
     const int r = blockIdx.x;
 
+    DSA_PHASE(1, 0);  // block start
     uint32_t key[KPT];
     load_keys<KPT>(P, vec, scores + (size_t)r * P, cand + (size_t)r * P, key);
     select_row<KPT, EXPAND, !PAIR && KPT <= 16>(r, P, Kw, key, sel, ex, sm);
+    DSA_PHASE(1, 7);  // stores issued
 }
 
 // Two stages for rows that are few and long, which a block each would leave most of the chip
