@@ -300,22 +300,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 }
 
 // Rows that all read one sequence's keys (prefill: consecutive positions of one sequence), as
-// a blocked product: block (g, c) scores rows 8g..8g+7 against pools [2048c, 2048c + 2048) in
-// sixteen tiles of 128 pools. A tile's keys are copied HBM->LDS (global_load_lds_dwordx4, each
-// pool row's 16-byte chunks XOR-rotated by the pool index so the 16 lanes of a fragment read
-// fall in distinct banks) into one of two buffers while the other is multiplied, and reused by
-// all 8 rows; wave w keeps the query fragments of rows 8g+2w and 8g+2w+1 in registers for the
-// whole block and runs, per 32-pool sub-tile, the two rows' 32-head x 32-pool products on
-// v_mfma_f32_32x32x16_bf16 from the same key fragments. Candidacy (the pool's flag and the
+// a blocked product: block (g, c) scores rows 16g..16g+15 against pools [2048c, 2048c + 2048)
+// in sixteen tiles of 128 pools. A tile's keys are copied HBM->LDS (global_load_lds_dwordx4,
+// each pool row's 16-byte chunks XOR-rotated by the pool index so the 16 lanes of a fragment
+// read fall in distinct banks) into one of two buffers while the other is multiplied, and
+// reused by all 16 rows (eight waves; with 8 rows and four waves a block the scorer took 290
+// against 283 us on prefill_2048_64k, the copies being twice as many); wave w keeps the query
+// fragments of rows 16g+2w and 16g+2w+1 in registers for the whole block and runs, per 32-pool
+// sub-tile, the two rows' 32-head x 32-pool products on v_mfma_f32_32x32x16_bf16 from the same
+// key fragments. Candidacy (the pool's flag and the
 // row's causal limit) and the relu-weighted head sum are the epilogue, as in the per-row form;
 // a tile's results are stored at the start of the next iteration, ahead of that iteration's
 // copies, so the wait that ends it finds them done.
-constexpr int kRB = 8;      // rows a block
+constexpr int kRB = 16;     // rows a block
+constexpr int kRBThreads = kRB * 32;  // two rows a wave
 constexpr int kCB = 128;    // pools a key tile
 constexpr int kTiles = 16;  // key tiles a block
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void index_scores_rowblock_kernel(
+__global__ __launch_bounds__(kRBThreads) __attribute__((amdgpu_waves_per_eu(2))) void index_scores_rowblock_kernel(
     int Q, int P, int Hi, int KP, int first_key, float scale, const uint16_t *__restrict__ q,
     const float *__restrict__ w, const int32_t *__restrict__ row_seq,
     const int32_t *__restrict__ row_pos, const void *__restrict__ keys,
@@ -326,8 +329,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks a key row
     constexpr int kTileBytes = kCB * kRowBytes;
     constexpr int kCopies = kTileBytes / 1024;       // wave-wide 1 KiB copies a tile
-    constexpr int kCopiesPerWave = kCopies / (kThreads / kWave);
-    static_assert(kCopies % (kThreads / kWave) == 0 && kCopiesPerWave >= 1, "tile copies");
+    constexpr int kCopiesPerWave = (kCopies + kRBThreads / kWave - 1) / (kRBThreads / kWave);
+    static_assert(kCopiesPerWave >= 1, "tile copies");
     constexpr int kSub = kCB / 32;                   // 32-pool sub-tiles a tile
     __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kTileBytes];
     __shared__ __attribute__((aligned(16))) float ks_s[2][kCB];
@@ -354,6 +357,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
         for (int k = 0; k < kCopiesPerWave; ++k) {
             const int d = wave * kCopiesPerWave + k;
+            if (d >= kCopies) break;  // uniform over the wave
             const int p = (1024 * d + 16 * lane) / kRowBytes;
             const int j = lane % kChunks;
             const int pg = min(p0 + p, P - 1);
@@ -379,7 +383,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // weights and limits (a row outside [0, Q) or of no sequence of the batch has none).
     issue_tile(0);
     // The block's flags (flags past P read as 0).
-    for (int i = tid; i < kCB * kTiles; i += kThreads) fl_s[i] = pbase + i < P ? pool_valid[pbase + i] : 0;
+    for (int i = tid; i < kCB * kTiles; i += kRBThreads) fl_s[i] = pbase + i < P ? pool_valid[pbase + i] : 0;
     if (tid < kRB * 32) {
         const int rl = tid / 32, h = tid % 32, r = g * kRB + rl;
         w_s[rl][h] = r < Q && h < Hi ? w[(size_t)r * Hi + h] : 0.0f;
@@ -492,7 +496,7 @@ hipError_t launch_rowblock_d(int Q, int P, int Hi, int KP, int first_key, float 
                              const uint8_t *pool_valid, float *scores, uint8_t *cand,
                              hipStream_t stream) {
     hipLaunchKernelGGL((index_scores_rowblock_kernel<D, FP8>),
-                       dim3((Q + kRB - 1) / kRB, (P + kCB * kTiles - 1) / (kCB * kTiles)), dim3(kThreads), 0, stream,
+                       dim3((Q + kRB - 1) / kRB, (P + kCB * kTiles - 1) / (kCB * kTiles)), dim3(kRBThreads), 0, stream,
                        Q, P, Hi, KP, first_key, scale, q, w, row_seq, row_pos, keys, key_scales,
                        pool_valid, scores, cand);
     return hipGetLastError();
@@ -585,7 +589,7 @@ hipError_t launch_index_scores_valid(int Q, int B, int P, int Hi, int D, int KP,
                                      const uint8_t *pool_valid, float *scores, uint8_t *cand,
                                      hipStream_t stream) {
     if (Q == 0 || P == 0) return hipSuccess;
-    // Many rows of one sequence (prefill): the row-blocked product, keys read once per 8 rows.
+    // Many rows of one sequence (prefill): the row-blocked product, keys read once per 16 rows.
     if (B == 1 && Q >= kRB) {
 #define DSA_ISR_CASE(d)                                                                         \
         if (D == d)                                                                             \

@@ -230,7 +230,7 @@ def test_compact_index_scores_more_rows_than_threads(name):
 
 @pytest.mark.parametrize("name", ["ragged_prefill", "ragged_fp8"])
 def test_compact_index_scores_rows_of_one_sequence(name):
-    """Many rows over one sequence take the row-blocked scorer (8 rows x 128 pools a block):
+    """Many rows over one sequence take the row-blocked scorer (16 rows x 128 pools a block):
     21 rows (a ragged row group) at random positions, some before first_key, one outside the
     batch, against the oracle; the pool count is not a multiple of 128."""
     di, x, _, _ = case(name)
